@@ -1,0 +1,355 @@
+"""Plain float64 CPU oracle of the GPTQ one-shot layer quantizer.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import or run this module. The HIP
+library neither imports it nor shares any code, table or helper with it.
+
+It follows the pages' definitions step by step, in their order and notation,
+with no blocking or fusion beyond what the method itself states. Sources
+(page title, then section):
+
+* aiqz.cc, "GPTQ：一键量化大模型压缩" -- sections 二阶信息 (Hessian),
+  逐层量化 (layer objective), 误差补偿 (OBS compensation δ_F),
+  分组方案 (per-group scale/zero), Python 演示 (a small damping term, per
+  output-neuron parameters, numpy round).
+* astro-blog-cod.pages.dev, LLM quantization techniques survey -- sections
+  1.2 量化原理 (x_q = round(x/s + z), dequant s(x_q - z)), 2.2 最优大脑量化
+  (OBS update), 2.3 GPTQ 的改进 (fixed column order, blocks of B = 128,
+  Cholesky).
+* compassingai.com, "GPTQ" concept page -- section 3 技術原理 (objective,
+  H = 2XX^T, per-column scale/zero chosen inside the sweep), section 4
+  關鍵引數 (bits 3/4/8; group 128 or -1 for "not grouped").
+* mcipr.com, "一文读懂GPTQ" -- section 三 (codes packed into 32-bit integer
+  arrays).
+* ai-papers.xuzou.cn reading card "GPTQ: Accurate Post-Training Quantization
+  for Generative Pre-trained Transformers" -- section 方法适配 (same order for
+  all rows so the inverse-Hessian information is shared; lazy batches of
+  B = 128 with the global update deferred to block end, same total compute;
+  Cholesky precomputation of the needed rows with mild damping).
+
+Readings taken where the pages are silent or disagree (each is also listed in
+the design notes of the repository):
+
+* H = 2 * sum_t x_t x_t^T, a sum over tokens, not a mean; X is tokens x
+  channels, so H = 2 X^T X.
+* Damping is relative: lambda = damp * mean(diag H), H_d = H + lambda I.
+* The rows of the inverse Hessian that drive the update are the rows of U,
+  the upper Cholesky factor of H_d^{-1} (H_d^{-1} = U^T U). Row q of U,
+  scaled by U_qq, is row q of the inverse of the not-yet-quantized
+  sub-Hessian, so the OBS step reads: err = w_q - what_q, e = err / U_qq,
+  w_j -= e * U_qj for j > q, loss += err^2 / (2 U_qq^2).
+* Quantizer: asymmetric min-max with an integer zero point, s = (xmax -
+  xmin)/(2^b - 1), z = rint(-xmin/s), code = clamp(rint(x/s) + z, 0, 2^b-1),
+  dequant = s (code - z); the range always includes 0 and an all-zero group
+  uses [-1, 1]. rint is round-half-to-even.
+* Group statistics come from the current (already compensated) values when
+  the sweep reaches the group's first column; group_size = -1 is one group
+  per row taken from the original row.
+* Blocks are exact: after a block, W[:, i2:] -= E U[i1:i2, i2:] applies the
+  deferred rank-1 updates, so any block size gives the same numbers up to
+  rounding. Grouping needs block % group == 0 or group % block == 0.
+* Packing: per row, an LSB-first bitstream along the columns; code j fills
+  bits [b j, b j + b) and word k holds bits [32 k, 32 k + 32); rows are
+  zero-padded to ceil(d_col b / 32) words.
+
+Every function here is pinned by the ``-m "not gpu"`` tests (brute force on
+tiny inputs, closed forms, invariants and hand-computed fixtures); none is
+parity-unpinned.
+"""
+
+from __future__ import annotations
+
+from typing import Iterable, Optional, Union
+
+import numpy as np
+
+F64 = np.float64
+
+
+class NotPositiveDefinite(np.linalg.LinAlgError):
+    """The damped Hessian has a non-positive Cholesky pivot."""
+
+
+# --------------------------------------------------------------------------
+# Stage 1: Hessian
+# --------------------------------------------------------------------------
+def hessian(chunks: Union[np.ndarray, Iterable[np.ndarray]], d: Optional[int] = None) -> np.ndarray:
+    """H = 2 * sum over tokens of x x^T, in float64.
+
+    aiqz.cc "GPTQ：一键量化大模型压缩", section 二阶信息: H is twice the sum of
+    the outer products of the layer's input vectors. compassingai.com
+    "GPTQ", section 3: H = 2XX^T with X holding one column per sample; the
+    arrays here hold one row per token, so the same matrix is 2 X^T X.
+
+    ``chunks`` is an array [n_tokens, d] or an iterable of such arrays; the
+    sum runs over all of them (a matmul per chunk is the library step).
+    """
+    if isinstance(chunks, np.ndarray):
+        chunks = [chunks]
+    H = None
+    for x in chunks:
+        x = np.asarray(x, dtype=F64)
+        if H is None:
+            H = np.zeros((x.shape[1], x.shape[1]), dtype=F64)
+        H += x.T @ x
+    if H is None:
+        H = np.zeros((d or 0, d or 0), dtype=F64)
+    return 2.0 * H
+
+
+# --------------------------------------------------------------------------
+# Stage 2: damping and the inverse-Hessian factor
+# --------------------------------------------------------------------------
+def damped(H: np.ndarray, damp: float):
+    """H_d = H + lambda I with lambda = damp * mean(diag H).
+
+    xuzou.cn reading card, section 方法适配: the Cholesky route is used with
+    a mild damping term; aiqz.cc, section Python 演示: a small multiple of the
+    identity is added before inversion. The relative form is the reading
+    used here.
+    """
+    H = np.asarray(H, dtype=F64)
+    lam = float(damp) * float(np.mean(np.diag(H))) if H.shape[0] else 0.0
+    return H + lam * np.eye(H.shape[0]), lam
+
+
+def _cholesky_lower(A: np.ndarray) -> np.ndarray:
+    try:
+        L = np.linalg.cholesky(A)
+    except np.linalg.LinAlgError as exc:
+        raise NotPositiveDefinite(str(exc)) from None
+    if not np.all(np.isfinite(L)) or (L.shape[0] and np.min(np.diag(L)) <= 0.0):
+        raise NotPositiveDefinite("non-positive pivot")
+    return L
+
+
+def prepare_hinv(H: np.ndarray, damp: float):
+    """Return (U, lambda): U upper triangular with H_d^{-1} = U^T U.
+
+    astro-blog survey, section 2.3 item 3, and xuzou.cn section 方法适配:
+    the rows of the inverse Hessian that the sweep needs are precomputed
+    with a Cholesky factorization of the damped matrix. Taken literally:
+    L = chol(H_d); H_d^{-1} = L^{-T} L^{-1}; U = chol(H_d^{-1})^T.
+    Raises NotPositiveDefinite if H_d has a non-positive pivot.
+    """
+    Hd, lam = damped(H, damp)
+    d = Hd.shape[0]
+    if d == 0:
+        return np.zeros((0, 0)), lam
+    L = _cholesky_lower(Hd)
+    Linv = np.linalg.inv(L)
+    Hinv = Linv.T @ Linv
+    U = _cholesky_lower(Hinv).T
+    return np.triu(U), lam
+
+
+# --------------------------------------------------------------------------
+# Quantizer
+# --------------------------------------------------------------------------
+def group_params(x: np.ndarray, bits: int, decide=F64):
+    """Per-row min-max scale and integer zero of a group of columns.
+
+    aiqz.cc, section 分组方案: scale = (max - min)/(2^bits - 1) and the zero
+    point maps the minimum to code 0; astro-blog survey, section 1.2: the
+    zero point z enters as round(x/s + z). The zero is rounded to an integer
+    code here. The range is widened to include 0 (so z is a valid code) and
+    an all-zero group uses [-1, 1].
+
+    ``x`` is [rows, cols]. Returns (s, z) as float64 arrays [rows]; z holds
+    integers. ``decide`` is the precision of the division and rounding
+    that fixes z (float64, or float32 to match a float32 implementation).
+    """
+    maxq = (1 << bits) - 1
+    xmin = np.minimum(np.min(x, axis=1), 0.0)
+    xmax = np.maximum(np.max(x, axis=1), 0.0)
+    dead = (xmin == 0.0) & (xmax == 0.0)
+    xmin = np.where(dead, -1.0, xmin)
+    xmax = np.where(dead, 1.0, xmax)
+    if decide == F64:
+        s = (xmax - xmin) / maxq
+        z = np.rint(-xmin / s)
+    else:
+        s32 = (xmax.astype(decide) - xmin.astype(decide)) / decide(maxq)
+        z = np.rint((-xmin.astype(decide)) / s32).astype(F64)
+        s = s32.astype(F64)
+    return s.astype(F64), z.astype(F64)
+
+
+def quantize_codes(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decide=F64) -> np.ndarray:
+    """code = clamp(rint(w/s) + z, 0, 2^b - 1) (astro-blog survey, 1.2)."""
+    maxq = (1 << bits) - 1
+    if decide == F64:
+        q = np.rint(w / s)
+    else:
+        q = np.rint(w.astype(decide) / s.astype(decide)).astype(F64)
+    return np.clip(q + z, 0, maxq)
+
+
+def rtn(W: np.ndarray, bits: int, group_size: int):
+    """Round-to-nearest baseline: every weight rounded on its own group grid.
+
+    aiqz.cc, section Python 演示 (the round-only baseline) and xuzou.cn,
+    section 证据 (RTN as the comparison). Group statistics come from the
+    original weights; there is no error compensation. Written without the
+    column loop so that it is an independent check of the sweep at H = I.
+    """
+    W = np.asarray(W, dtype=F64)
+    d_row, d_col = W.shape
+    g = d_col if group_size == -1 else group_size
+    n_groups = 1 if group_size == -1 else -(-d_col // group_size)
+    codes = np.zeros((d_row, d_col), dtype=np.int64)
+    scales = np.zeros((d_row, n_groups))
+    zeros = np.zeros((d_row, n_groups))
+    for k in range(n_groups):
+        sl = slice(k * g, min(d_col, (k + 1) * g))
+        s, z = group_params(W[:, sl], bits)
+        scales[:, k], zeros[:, k] = s, z
+        codes[:, sl] = quantize_codes(W[:, sl], s[:, None], z[:, None], bits)
+    return codes.astype(np.uint8), scales, zeros
+
+
+def dequantize(codes, scales, zeros, group_size: int) -> np.ndarray:
+    """what = s (code - z), with the group of column j being j // g."""
+    codes = np.asarray(codes, dtype=F64)
+    d_col = codes.shape[1]
+    if group_size == -1:
+        gi = np.zeros(d_col, dtype=np.int64)
+    else:
+        gi = np.arange(d_col) // group_size
+    return np.asarray(scales, F64)[:, gi] * (codes - np.asarray(zeros, F64)[:, gi])
+
+
+# --------------------------------------------------------------------------
+# Stage 3: fixed-order column sweep with OBS compensation and lazy blocks
+# --------------------------------------------------------------------------
+def quantize_layer(
+    W: np.ndarray,
+    U: np.ndarray,
+    bits: int,
+    group_size: int,
+    block: int = 128,
+    decide=F64,
+):
+    """GPTQ sweep of one layer, columns in natural order.
+
+    * aiqz.cc, section 误差补偿: after a column is rounded, the remaining
+      columns of the same row absorb the error through the inverse Hessian,
+      delta_F = (q - w_q)/[H^-1]_qq [H^-1]_{F,q}.
+    * astro-blog survey, section 2.3 items 1-3 and xuzou.cn, section
+      方法适配: a fixed order shared by all rows, blocks of B columns whose
+      global update waits until the block is done, inverse rows from a
+      Cholesky factor (here the rows of U).
+    * compassingai.com "GPTQ", section 3: scale and zero are chosen inside
+      the sweep, before a column is rounded.
+
+    W is [d_row, d_col] (any float dtype; upcast exactly to float64). U is
+    [d_col, d_col] upper triangular. Returns a dict with codes (uint8),
+    scales, zeros (float64, integer-valued), Wq (the dequantized weights),
+    row_loss and loss (sum over columns of err^2 / (2 U_qq^2)), and packed.
+    ``decide`` is the precision in which each code is decided (float64 by
+    default; float32 reproduces the decision of a float32 implementation
+    given the same inputs).
+    """
+    W = np.array(W, dtype=F64, copy=True)
+    U = np.asarray(U, dtype=F64)
+    d_row, d_col = W.shape
+    if U.shape != (d_col, d_col):
+        raise ValueError("U must be [d_col, d_col]")
+    if bits not in (2, 3, 4, 8):
+        raise ValueError("bits must be 2, 3, 4 or 8")
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    if group_size != -1:
+        if group_size < 1 or (block % group_size and group_size % block):
+            raise ValueError("need block % group == 0 or group % block == 0")
+    n_groups = 1 if group_size == -1 else -(-d_col // group_size)
+    codes = np.zeros((d_row, d_col), dtype=np.uint8)
+    scales = np.zeros((d_row, n_groups))
+    zeros = np.zeros((d_row, n_groups))
+    Wq = np.zeros((d_row, d_col))
+    row_loss = np.zeros(d_row)
+
+    if group_size == -1 and d_col:
+        s, z = group_params(W, bits, decide)
+        scales[:, 0], zeros[:, 0] = s, z
+
+    for i1 in range(0, d_col, block):
+        i2 = min(i1 + block, d_col)
+        E = np.zeros((d_row, i2 - i1))
+        for q in range(i1, i2):
+            if group_size != -1 and q % group_size == 0:
+                k = q // group_size
+                s, z = group_params(W[:, q : min(q + group_size, d_col)], bits, decide)
+                scales[:, k], zeros[:, k] = s, z
+            w = W[:, q]
+            c = quantize_codes(w, s, z, bits, decide)
+            what = s * (c - z)
+            err = w - what
+            d = U[q, q]
+            row_loss += err * err / (2.0 * d * d)
+            e = err / d
+            W[:, q + 1 : i2] -= np.outer(e, U[q, q + 1 : i2])
+            E[:, q - i1] = e
+            codes[:, q] = c.astype(np.uint8)
+            Wq[:, q] = what
+        if i2 < d_col:
+            W[:, i2:] -= E @ U[i1:i2, i2:]
+
+    return dict(
+        codes=codes,
+        scales=scales,
+        zeros=zeros,
+        Wq=Wq,
+        row_loss=row_loss,
+        loss=float(np.sum(row_loss)),
+        packed=pack(codes, bits),
+    )
+
+
+def layer_loss_direct(X: np.ndarray, W: np.ndarray, Wq: np.ndarray, lam: float = 0.0) -> float:
+    """||X (W - Wq)^T||_F^2 + (lambda/2) ||W - Wq||_F^2.
+
+    aiqz.cc, section 逐层量化: the layer objective is the squared Frobenius
+    norm of the output difference. With H_d = 2 X^T X + lambda I the sum of
+    the sweep's per-column losses equals half the H_d-weighted error
+    quadratic, which is this quantity.
+    """
+    D = np.asarray(W, F64) - np.asarray(Wq, F64)
+    Y = np.asarray(X, F64) @ D.T
+    return float(np.sum(Y * Y) + 0.5 * lam * np.sum(D * D))
+
+
+# --------------------------------------------------------------------------
+# Packing
+# --------------------------------------------------------------------------
+def words_per_row(d_col: int, bits: int) -> int:
+    return -(-d_col * bits // 32)
+
+
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """b-bit codes -> uint32 words, per row an LSB-first bitstream.
+
+    mcipr.com "一文读懂GPTQ", section 三: low-bit codes are stored in 32-bit
+    integer arrays. Bit i of a row's stream is bit (i mod b) of code i // b;
+    word k holds stream bits [32k, 32k + 32).
+    """
+    codes = np.asarray(codes, dtype=np.uint64)
+    d_row, d_col = codes.shape
+    nw = words_per_row(d_col, bits)
+    bitpos = np.arange(bits, dtype=np.uint64)
+    stream = ((codes[:, :, None] >> bitpos) & np.uint64(1)).reshape(d_row, d_col * bits)
+    padded = np.zeros((d_row, nw * 32), dtype=np.uint64)
+    padded[:, : d_col * bits] = stream
+    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)
+    words = (padded.reshape(d_row, nw, 32) * weights).sum(axis=2)
+    return words.astype(np.uint32)
+
+
+def unpack(words: np.ndarray, d_col: int, bits: int) -> np.ndarray:
+    """Inverse of ``pack``."""
+    words = np.asarray(words, dtype=np.uint64)
+    d_row, nw = words.shape
+    stream = ((words[:, :, None] >> np.arange(32, dtype=np.uint64)) & np.uint64(1)).reshape(d_row, nw * 32)
+    stream = stream[:, : d_col * bits].reshape(d_row, d_col, bits)
+    vals = (stream << np.arange(bits, dtype=np.uint64)).sum(axis=2)
+    return vals.astype(np.uint8)
