@@ -1,0 +1,242 @@
+"""Benchmark of the GPTQ layer path on one MI355X.
+
+One step is the whole layer path on device-resident inputs:
+  H = 2 X^T X (gptq_hessian_accumulate), U = chol((H + lambda I)^-1)
+  (gptq_prepare_hinv), and the column sweep with packing and loss
+  (gptq_quantize_layer).
+Default workload: the 4096 x 4096 fp16 attention-projection layer with
+128 x 2048 = 262144 fp16 calibration tokens, 4-bit, group 128, damp 0.01,
+B = 128 (seeded synthetic inputs standing in for C4 activations).
+
+Prints one JSON line. `value` is weight columns quantized per second for
+the whole layer path (d_col / step time); per-stage times, the Hessian
+TFLOP/s, the roofline of the dominant stage and the float64 oracle's rate
+on this machine's CPU cores are reported beside it.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ layer quantize time (ms) + weight-cols/s; Hessian SYRK TFLOP/s, % peak"
+PEAK_FP16_MFMA = 2.5e15  # dense fp16 MFMA, MI355X
+PEAK_FP32_MFMA = 157.3e12
+PEAK_FP64_MFMA = 78.6e12
+PEAK_HBM = 8.0e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def upload_activations(cfg, torch, dev):
+    from workload import activation_chunks
+
+    X = torch.empty((cfg.n_tokens, cfg.d_col), dtype=getattr(torch, cfg.x_dtype), device=dev)
+    t = 0
+    for ch in activation_chunks(cfg, threads=min(16, os.cpu_count() or 8)):
+        X[t : t + ch.shape[0]].copy_(torch.from_numpy(ch))
+        t += ch.shape[0]
+    return X
+
+
+def cpu_baseline(cfg, budget_rows=128, budget_tokens=16384):
+    """The float64 oracle timed on a bounded sample of the same layer.
+
+    Sample: the Hessian of the first `budget_tokens` tokens (time scaled by
+    n_tokens / budget_tokens, the cost being linear in tokens), the damped
+    factor of that Hessian at full width, and the sweep of `budget_rows`
+    rows (time scaled by d_row / budget_rows; rows are independent).
+    """
+    import oracle.gptq_oracle as O
+    from workload import activation_chunks, weights
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    chunks = []
+    got = 0
+    for ch in activation_chunks(cfg, threads=4):
+        chunks.append(ch)
+        got += ch.shape[0]
+        if got >= budget_tokens:
+            break
+    Xs = np.concatenate(chunks)[:budget_tokens]
+    rows = np.arange(min(budget_rows, cfg.d_row))
+    Ws = weights(cfg, rows=rows)
+    t0 = time.perf_counter()
+    H = O.hessian([Xs[i : i + 4096] for i in range(0, len(Xs), 4096)])
+    t1 = time.perf_counter()
+    U, _ = O.prepare_hinv(H, cfg.damp)
+    t2 = time.perf_counter()
+    O.quantize_layer(Ws, U, cfg.bits, cfg.group_size, cfg.block)
+    t3 = time.perf_counter()
+    t_h = (t1 - t0) * cfg.n_tokens / len(Xs)
+    t_u = t2 - t1
+    t_q = (t3 - t2) * cfg.d_row / len(rows)
+    total = t_h + t_u + t_q
+    return {
+        "value": cfg.d_col / total,
+        "unit": "weight-cols/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (
+            f"float64 numpy oracle: Hessian of {len(Xs)} of {cfg.n_tokens} tokens (x{cfg.n_tokens / len(Xs):.0f}), "
+            f"full-width damped factor, sweep of {len(rows)} of {cfg.d_row} rows (x{cfg.d_row / len(rows):.0f}); "
+            f"measured {t3 - t0:.1f} s, extrapolated layer time {total:.1f} s"
+        ),
+        "stage_s": {"hessian": t_h, "hinv": t_u, "quantize": t_q},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="attn_proj_4096x4096_4bit_g128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(
+            f"bench.py measures one GPU: the GPTQ layer path here runs on a single MI355X "
+            f"(--gpus {args.gpus} is not supported; multi-GPU sharding is described in DESIGN.md)",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import post_weight_quantization_17_amd as g
+    from workload import CONFIGS, weights
+
+    g.load()
+    cfg = CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"bench: {cfg.name}: W {cfg.d_row}x{cfg.d_col} {cfg.w_dtype}, X {cfg.n_tokens}x{cfg.d_col} {cfg.x_dtype}")
+    t0 = time.perf_counter()
+    X = upload_activations(cfg, torch, dev)
+    W = torch.from_numpy(weights(cfg)).to(dev)
+    torch.cuda.synchronize()
+    log(f"bench: inputs resident in HBM after {time.perf_counter() - t0:.1f} s")
+
+    d, n = cfg.d_col, cfg.n_tokens
+    ws_h = torch.empty(g.gptq_hessian_workspace_size(n, d, X.dtype), dtype=torch.uint8, device=dev)
+    ws_u = torch.empty(g.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(
+        g.gptq_quantize_layer_workspace_size(cfg.d_row, d, cfg.bits, cfg.group_size, cfg.block), dtype=torch.uint8, device=dev
+    )
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    hv = g.Hinv(
+        torch.empty((d, d), dtype=torch.float32, device=dev),
+        torch.empty((), dtype=torch.float32, device=dev),
+        torch.empty((), dtype=torch.int32, device=dev),
+    )
+    eye = torch.eye(d, dtype=torch.float32, device=dev)
+    q = g.gptq_quantize_layer(W, eye, cfg.bits, cfg.group_size, cfg.block, ws=ws_q)  # allocates the outputs once
+    del eye
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        g.gptq_hessian_accumulate(X, H=H, ws=ws_h)
+        if ev:
+            ev[1].record()
+        g.gptq_prepare_hinv(H, cfg.damp, ws=ws_u, out=hv)
+        if ev:
+            ev[2].record()
+        g.gptq_quantize_layer(W, hv.U, cfg.bits, cfg.group_size, cfg.block, ws=ws_q, out=q)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(hv.info.item()) != 0:
+        raise RuntimeError(f"factorization failed: info={int(hv.info.item())}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        step(evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(end) / args.steps
+    t_h = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_u = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_q = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    log(f"bench: {args.steps} steps in {wall:.3f} s wall; per step {ms:.3f} ms (H {t_h:.3f}, U {t_u:.3f}, Q {t_q:.3f})")
+
+    syrk_flops = float(n) * d * (d + 1)
+    syrk_tflops = syrk_flops / (t_h * 1e-3) / 1e12
+    trail_flops = float(sum(2.0 * cfg.d_row * cfg.block * (d - i2) for i2 in range(cfg.block, d, cfg.block)))
+    chol_flops = 2.0 * d**3 / 3.0
+    roofline = {
+        "bound": "mfma",
+        "kernel": "Hessian SYRK stage (syrk_f16_mfma + fixed-order split reduction)",
+        "achieved": syrk_tflops,
+        "peak": PEAK_FP16_MFMA / 1e12,
+        "unit": "TFLOP/s",
+        "frac": syrk_tflops * 1e12 / PEAK_FP16_MFMA,
+        "traffic": None,
+        "per_launch_flops": syrk_flops,
+    }
+    out = {
+        "metric": METRIC,
+        "value": d / (ms * 1e-3),
+        "unit": "weight-cols/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 in / f32 accumulate (H); f64 (factor); f32 (sweep)",
+        "data": "synthetic (seeded; stands in for C4 activations and real weights)",
+        "config": {
+            "workload": cfg.name,
+            "d_row": cfg.d_row,
+            "d_col": d,
+            "n_tokens": n,
+            "bits": cfg.bits,
+            "group_size": cfg.group_size,
+            "block": cfg.block,
+            "damp": cfg.damp,
+        },
+        "stages_ms": {"hessian": t_h, "prepare_hinv": t_u, "quantize_layer": t_q},
+        "quantize_layer_ms": t_q,
+        "quantize_weight_cols_per_s": d / (t_q * 1e-3),
+        "hessian_tflops": syrk_tflops,
+        "hessian_pct_fp16_peak": 100.0 * syrk_tflops * 1e12 / PEAK_FP16_MFMA,
+        "prepare_hinv_tflops_fp64": chol_flops / (t_u * 1e-3) / 1e12,
+        "quantize_trailing_tflops_lower_bound": trail_flops / (t_q * 1e-3) / 1e12,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the float64 oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

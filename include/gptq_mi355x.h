@@ -1,0 +1,169 @@
+/*
+ * gptq_mi355x.h -- C ABI of the GPTQ one-shot layer quantizer for MI355X
+ * (gfx950).
+ *
+ * The library computes the three stages of the GPTQ layer path:
+ *   1. H (+)= 2 X^T X              gptq_hessian_accumulate
+ *   2. U = chol((H + lambda I)^-1)  gptq_prepare_hinv     (upper factor)
+ *   3. the fixed-order column sweep with OBS compensation, lazy blocks,
+ *      per-group min-max scale/zero and packed b-bit codes
+ *                                   gptq_quantize_layer (+ gptq_pack_codes)
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as device pointers refer to GPU memory the caller
+ *     allocated (for instance with torch). The library never allocates,
+ *     frees or retains caller memory; it keeps no state between calls.
+ *   - All matrices are row-major and contiguous unless a leading dimension
+ *     is given.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on that stream and returns; nothing is
+ *     synchronized. Results are valid once the stream has reached them.
+ *   - Argument errors are reported synchronously, before anything is
+ *     enqueued, as a gptq_status. A failed kernel launch returns
+ *     GPTQ_E_HIP. Numerical breakdown of the factorization is reported on
+ *     the device through `info`.
+ *   - `ws`/`ws_bytes`: device scratch the caller provides, at least the size
+ *     the matching *_workspace_size function returns; its contents on entry
+ *     do not matter and on exit are unspecified. Two calls that may run at
+ *     the same time need separate workspaces.
+ *   - Sizes are int64_t; a size of 0 is allowed where stated and then does
+ *     nothing.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_E_INVALID_ARG = 1, /* a size, pointer or parameter is out of range   */
+  GPTQ_E_UNSUPPORTED = 2, /* valid for the method but not implemented here  */
+  GPTQ_E_WORKSPACE = 3,   /* ws_bytes smaller than the required size         */
+  GPTQ_E_HIP = 4          /* a HIP launch or runtime call failed             */
+} gptq_status;
+
+typedef enum { GPTQ_F16 = 0, GPTQ_F32 = 1 } gptq_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* gptq_status_string(int status);
+
+/* Library version as "major.minor.patch" (static storage). */
+const char* gptq_version(void);
+
+/* ------------------------------------------------------------------------
+ * Stage 1 -- Hessian of the layer objective.
+ *
+ * Defines: H = 2 * sum over tokens t of x_t x_t^T (aiqz.cc "GPTQ：一键量化
+ * 大模型压缩", section 二阶信息; compassingai.com "GPTQ", section 3, H = 2XX^T
+ * with samples as columns). Here X holds one token per row, so H = 2 X^T X.
+ *
+ *   X          device, n_tokens x d, element type xdtype (GPTQ_F16 or
+ *              GPTQ_F32), row stride ldx >= d elements.
+ *   H          device fp32 d x d; both triangles are written.
+ *   accumulate 0: H = 2 X^T X.  1: H += 2 X^T X (calibration in chunks).
+ * The products of fp16 inputs are exact in fp32; partial sums are fp32
+ * and are combined in a fixed order, so the result is deterministic.
+ * n_tokens = 0 writes zeros (accumulate = 0) or leaves H unchanged.
+ * Errors: d < 1, n_tokens < 0, ldx < d, NULL X (with n_tokens > 0) or H,
+ * unknown dtype -> GPTQ_E_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+size_t gptq_hessian_workspace_size(int64_t n_tokens, int64_t d, int xdtype);
+int gptq_hessian_accumulate(const void* X, int xdtype, int64_t n_tokens, int64_t d, int64_t ldx,
+                            float* H, int accumulate, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 2 -- the rows of the inverse Hessian that the sweep uses.
+ *
+ * Defines: with mild damping, a Cholesky factorization precomputes the
+ * needed rows of H^-1 (astro-blog LLM quantization survey, section 2.3
+ * item 3; xuzou.cn reading card of the GPTQ paper, section 方法适配).
+ * Computes lambda = damp * mean(diag H) (damp is the relative fraction),
+ * H_d = H + lambda I, and U: upper triangular with positive diagonal and
+ * H_d^-1 = U^T U. Row q of U, times U_qq, is row q of the inverse of the
+ * trailing sub-Hessian H_d[q:, q:].
+ *
+ *   H          device fp32 d x d, symmetric (only the lower triangle is
+ *              read); not modified.
+ *   U          device fp32 d x d; the strictly lower triangle is zeroed.
+ *   lambda_out device fp32 scalar, may be NULL.
+ *   info       device int32 scalar: 0 on success; k > 0 if H_d is not
+ *              numerically positive definite, k - 1 being the column (in H's
+ *              indexing) where the factorization broke down. U is then
+ *              unspecified.
+ * The factorization runs in fp64 on the device. Errors: d < 1, NULL H, U
+ * or info, damp < 0 or not finite -> GPTQ_E_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+size_t gptq_prepare_hinv_workspace_size(int64_t d);
+int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* lambda_out,
+                      int32_t* info, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 3 -- fixed-order GPTQ column sweep.
+ *
+ * Defines: columns in natural order, shared by all rows; each rounded
+ * column's error is spread over the row's remaining columns through the
+ * inverse Hessian (aiqz.cc, section 误差补偿; astro-blog survey, sections
+ * 2.2-2.3); blocks of `block` columns whose update of later columns is
+ * deferred to the end of the block (xuzou.cn, section 方法适配);
+ * per-group asymmetric min-max scale and zero (aiqz.cc, section 分组方案;
+ * astro-blog survey, section 1.2); codes packed into 32-bit words
+ * (mcipr.com "一文读懂GPTQ", section 三). For every row and column q:
+ *   at a group start: xmin = min(0, min of the group's current values),
+ *     xmax = max(0, ...) ([-1, 1] if both are 0); s = (xmax - xmin)/maxq,
+ *     z = rint(-xmin / s); group_size = -1 takes one group per row from
+ *     the original row.
+ *   code = clamp(rint(w_q / s) + z, 0, maxq), what = s (code - z),
+ *   err = w_q - what, e = err / U_qq, w_j -= e U_qj for j > q,
+ *   loss += err^2 / (2 U_qq^2)            (maxq = 2^bits - 1)
+ * Arithmetic is fp32 (code decisions included) with the loss in fp64.
+ *
+ *   W          device, d_row x d_col, wdtype GPTQ_F16 or GPTQ_F32; read only.
+ *   U          device fp32 d_col x d_col from gptq_prepare_hinv (only the
+ *              upper triangle is read).
+ *   bits       2, 3, 4 or 8.
+ *   group_size -1, or a multiple of 16 with block % group_size == 0 or
+ *              group_size % block == 0.
+ *   block      128 (the lazy-batch width; other widths -> UNSUPPORTED).
+ *   codes      device uint8 d_row x d_col (code per weight).
+ *   scales     device fp32 d_row x n_groups, zeros device int32 d_row x
+ *              n_groups, n_groups = 1 if group_size == -1 else
+ *              ceil(d_col / group_size).
+ *   packed     device uint32 d_row x ceil(d_col * bits / 32): per row an
+ *              LSB-first bitstream, code j in bits [bits j, bits j + bits),
+ *              zero padded.
+ *   loss       device fp64 scalar (sum over rows and columns).
+ *   row_loss   device fp32 d_row, may be NULL.
+ * Errors: sizes < 1, NULL outputs (row_loss excepted), bad bits or group
+ * -> GPTQ_E_INVALID_ARG; block != 128 -> GPTQ_E_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int bits,
+                                          int64_t group_size, int64_t block);
+int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U,
+                        int bits, int64_t group_size, int64_t block, uint8_t* codes,
+                        float* scales, int32_t* zeros, uint32_t* packed, double* loss,
+                        float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Packing of existing codes (the same device routine the sweep uses).
+ *
+ * Defines: b-bit codes stored in 32-bit integer arrays (mcipr.com
+ * "一文读懂GPTQ", section 三); layout as for `packed` above. Codes are
+ * masked to their low `bits` bits.
+ *   codes  device uint8 d_row x d_col;  packed device uint32 d_row x
+ *   ceil(d_col * bits / 32).
+ * Errors: sizes < 1, NULL pointers, bits not in {2,3,4,8}
+ * -> GPTQ_E_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+int gptq_pack_codes(const uint8_t* codes, int64_t d_row, int64_t d_col, int bits,
+                    uint32_t* packed, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

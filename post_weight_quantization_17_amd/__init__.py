@@ -1,0 +1,255 @@
+"""Python binding of the gfx950 GPTQ layer library (libgptq_mi355x.so).
+
+The functions here have the names of the C entry points declared in
+``include/gptq_mi355x.h`` and only marshal arguments: they check tensor
+devices, dtypes and shapes, allocate outputs and workspaces with torch, and
+pass raw device pointers plus torch's current HIP stream to the library.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback path, and loading fails loudly if the library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgptq_mi355x.so")
+
+GPTQ_OK, GPTQ_E_INVALID_ARG, GPTQ_E_UNSUPPORTED, GPTQ_E_WORKSPACE, GPTQ_E_HIP = range(5)
+GPTQ_F16, GPTQ_F32 = 0, 1
+
+_lib: Optional[ctypes.CDLL] = None
+
+_c_size, _c_i64, _c_int, _c_dbl, _c_ptr = ctypes.c_size_t, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+
+_SIGNATURES = {
+    "gptq_status_string": (ctypes.c_char_p, [_c_int]),
+    "gptq_version": (ctypes.c_char_p, []),
+    "gptq_hessian_workspace_size": (_c_size, [_c_i64, _c_i64, _c_int]),
+    "gptq_hessian_accumulate": (_c_int, [_c_ptr, _c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "gptq_prepare_hinv_workspace_size": (_c_size, [_c_i64]),
+    "gptq_prepare_hinv": (_c_int, [_c_ptr, _c_i64, _c_dbl, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "gptq_quantize_layer_workspace_size": (_c_size, [_c_i64, _c_i64, _c_int, _c_i64, _c_i64]),
+    "gptq_quantize_layer": (
+        _c_int,
+        [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr],
+    ),
+    "gptq_pack_codes": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr]),
+}
+
+
+class GptqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build the HIP library first "
+            "(python -m post_weight_quantization_17_amd.build)"
+        )
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gptq_status_string(status).decode()
+
+
+def version() -> str:
+    return load().gptq_version().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != GPTQ_OK:
+        raise GptqError(fn, status)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return GPTQ_F16
+    if t.dtype == torch.float32:
+        return GPTQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float16 or float32)")
+
+
+def _on_gpu(name: str, t: torch.Tensor) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None and ws.numel() * ws.element_size() >= nbytes:
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- stage 1
+def gptq_hessian_workspace_size(n_tokens: int, d: int, dtype: torch.dtype) -> int:
+    return load().gptq_hessian_workspace_size(n_tokens, d, GPTQ_F16 if dtype == torch.float16 else GPTQ_F32)
+
+
+def gptq_hessian_accumulate(
+    X: torch.Tensor, H: Optional[torch.Tensor] = None, accumulate: bool = False, ws: Optional[torch.Tensor] = None
+) -> torch.Tensor:
+    """H (+)= 2 X^T X for X [n_tokens, d] (fp16/fp32, rows may be strided)."""
+    _on_gpu("X", X)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    n, d = X.shape
+    if H is None:
+        if accumulate:
+            raise ValueError("accumulate needs an existing H")
+        H = torch.empty((d, d), dtype=torch.float32, device=X.device)
+    if H.shape != (d, d) or H.dtype != torch.float32 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 [d, d] tensor")
+    lib = load()
+    code = _dtype_code(X)
+    need = lib.gptq_hessian_workspace_size(n, d, code)
+    ws = _workspace(need, X.device, ws)
+    ldx = X.stride(0) if n > 1 else d
+    _check(
+        "gptq_hessian_accumulate",
+        lib.gptq_hessian_accumulate(_ptr(X), code, n, d, ldx, _ptr(H), int(accumulate), _ptr(ws), ws.numel(), _stream()),
+    )
+    return H
+
+
+# ---------------------------------------------------------------- stage 2
+@dataclasses.dataclass
+class Hinv:
+    U: torch.Tensor  # fp32 [d, d] upper triangular, H_d^-1 = U^T U
+    lam: torch.Tensor  # fp32 scalar (device)
+    info: torch.Tensor  # int32 scalar (device), 0 = success
+
+
+def gptq_prepare_hinv_workspace_size(d: int) -> int:
+    return load().gptq_prepare_hinv_workspace_size(d)
+
+
+def gptq_prepare_hinv(
+    H: torch.Tensor,
+    damp: float = 0.01,
+    U: Optional[torch.Tensor] = None,
+    ws: Optional[torch.Tensor] = None,
+    out: Optional[Hinv] = None,
+) -> Hinv:
+    """Upper Cholesky factor U of (H + damp*mean(diag H) I)^-1."""
+    _on_gpu("H", H)
+    if H.dim() != 2 or H.shape[0] != H.shape[1] or H.dtype != torch.float32 or not H.is_contiguous():
+        raise ValueError("H must be a contiguous float32 square tensor")
+    d = H.shape[0]
+    if out is not None:
+        U, lam, info = out.U, out.lam, out.info
+    else:
+        if U is None:
+            U = torch.empty((d, d), dtype=torch.float32, device=H.device)
+        lam = torch.empty((), dtype=torch.float32, device=H.device)
+        info = torch.empty((), dtype=torch.int32, device=H.device)
+    lib = load()
+    ws = _workspace(lib.gptq_prepare_hinv_workspace_size(d), H.device, ws)
+    _check(
+        "gptq_prepare_hinv",
+        lib.gptq_prepare_hinv(_ptr(H), d, float(damp), _ptr(U), _ptr(lam), _ptr(info), _ptr(ws), ws.numel(), _stream()),
+    )
+    return Hinv(U, lam, info)
+
+
+# ---------------------------------------------------------------- stage 3
+@dataclasses.dataclass
+class Quantized:
+    codes: torch.Tensor  # uint8 [d_row, d_col]
+    scales: torch.Tensor  # fp32 [d_row, n_groups]
+    zeros: torch.Tensor  # int32 [d_row, n_groups]
+    packed: torch.Tensor  # int32 view of the uint32 words [d_row, ceil(d_col*bits/32)]
+    loss: torch.Tensor  # fp64 scalar
+    row_loss: Optional[torch.Tensor]  # fp32 [d_row]
+
+
+def n_groups(d_col: int, group_size: int) -> int:
+    return 1 if group_size == -1 else -(-d_col // group_size)
+
+
+def words_per_row(d_col: int, bits: int) -> int:
+    return -(-d_col * bits // 32)
+
+
+def gptq_quantize_layer_workspace_size(d_row: int, d_col: int, bits: int, group_size: int, block: int = 128) -> int:
+    return load().gptq_quantize_layer_workspace_size(d_row, d_col, bits, group_size, block)
+
+
+def gptq_quantize_layer(
+    W: torch.Tensor,
+    U: torch.Tensor,
+    bits: int,
+    group_size: int,
+    block: int = 128,
+    want_row_loss: bool = True,
+    ws: Optional[torch.Tensor] = None,
+    out: Optional[Quantized] = None,
+) -> Quantized:
+    """GPTQ sweep of W [d_row, d_col] (fp16/fp32) with the factor U."""
+    _on_gpu("W", W)
+    _on_gpu("U", U)
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D tensor")
+    d_row, d_col = W.shape
+    if U.shape != (d_col, d_col) or U.dtype != torch.float32 or not U.is_contiguous():
+        raise ValueError("U must be a contiguous float32 [d_col, d_col] tensor")
+    dev = W.device
+    if out is None:
+        ng = n_groups(d_col, group_size) if group_size == -1 or group_size > 0 else 1
+        out = Quantized(
+            codes=torch.empty((d_row, d_col), dtype=torch.uint8, device=dev),
+            scales=torch.empty((d_row, ng), dtype=torch.float32, device=dev),
+            zeros=torch.empty((d_row, ng), dtype=torch.int32, device=dev),
+            packed=torch.empty((d_row, words_per_row(d_col, bits)), dtype=torch.int32, device=dev),
+            loss=torch.empty((), dtype=torch.float64, device=dev),
+            row_loss=torch.empty((d_row,), dtype=torch.float32, device=dev) if want_row_loss else None,
+        )
+    lib = load()
+    ws = _workspace(lib.gptq_quantize_layer_workspace_size(d_row, d_col, bits, group_size, block), dev, ws)
+    _check(
+        "gptq_quantize_layer",
+        lib.gptq_quantize_layer(
+            _ptr(W), _dtype_code(W), d_row, d_col, _ptr(U), bits, group_size, block,
+            _ptr(out.codes), _ptr(out.scales), _ptr(out.zeros), _ptr(out.packed), _ptr(out.loss),
+            _ptr(out.row_loss), _ptr(ws), ws.numel(), _stream(),
+        ),
+    )
+    return out
+
+
+def gptq_pack_codes(codes: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pack uint8 codes [d_row, d_col] into int32 (bit pattern uint32) words."""
+    _on_gpu("codes", codes)
+    if codes.dtype != torch.uint8 or codes.dim() != 2 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous uint8 2-D tensor")
+    d_row, d_col = codes.shape
+    if packed is None:
+        packed = torch.empty((d_row, words_per_row(d_col, bits)), dtype=torch.int32, device=codes.device)
+    _check("gptq_pack_codes", load().gptq_pack_codes(_ptr(codes), d_row, d_col, bits, _ptr(packed), _stream()))
+    return packed

@@ -1,0 +1,355 @@
+// Stage 1 of the GPTQ layer path: H (+)= 2 X^T X.
+//
+// aiqz.cc "GPTQ：一键量化大模型压缩", section 二阶信息: the Hessian of the layer
+// objective is twice the sum over calibration inputs of x x^T. X arrives as
+// tokens x channels, so H = 2 X^T X: a symmetric rank-N update whose
+// reduction runs over tokens.
+//
+// Design (gfx950):
+//  * Only upper 256x256 tiles (bi <= bj) are computed. Each workgroup
+//    (4 waves, 2x2, each wave 128x128 = 4x4 MFMA 32x32x16 f16 tiles) owns one
+//    tile for one contiguous token range (split-K).
+//  * X tiles are read from HBM with 16-byte loads along channels (8 tokens
+//    x 8 channels per thread), transposed in registers with v_perm so each
+//    channel's 8 consecutive tokens form one 16-byte LDS chunk, and stored in
+//    a swizzled [channel][32 tokens] LDS layout. MFMA operands for both sides
+//    are then single ds_read_b128 per lane. Two LDS stages double-buffer the
+//    token loop; global loads of step k+1 overlap the MFMAs of step k.
+//  * fp16 products are exact in fp32 and MFMA accumulates in fp32. Each
+//    split writes its partial tile to the workspace; a second kernel sums the
+//    splits in a fixed order in fp64, scales by 2, mirrors the upper tiles
+//    into both triangles and applies accumulate. No atomics: deterministic.
+//  * fp32 inputs take a plain VALU tile kernel (64x64 tiles, same partials
+//    and reduction).
+#include "gptq_common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int SY_T = 256;         // tile edge (fp16 MFMA kernel)
+constexpr int SY_BK = 32;         // tokens per LDS stage
+constexpr int SY_THREADS = 256;
+constexpr int SYF_T = 64;         // tile edge (fp32 VALU kernel)
+constexpr int SYF_BK = 16;
+
+// Upper-triangle tile index -> (bi, bj), row-major over bi <= bj.
+__device__ __forceinline__ void tile_coords(int tile, int nb, int& bi, int& bj) {
+  int r = 0, t = tile;
+  while (t >= nb - r) {
+    t -= nb - r;
+    ++r;
+  }
+  bi = r;
+  bj = r + t;
+}
+
+// LDS byte offset of the 16-byte chunk holding tokens [8 to, 8 to + 8) of
+// channel ch inside one [256 channel][32 token] fp16 panel. The row
+// permutation and chunk XOR keep both the transposing writes (channels
+// 8c+v, c varying) and the MFMA fragment reads (32 consecutive channels)
+// spread over distinct banks.
+__device__ __forceinline__ int panel_off(int ch, int to) {
+  const int row = ch ^ ((ch >> 3) & 3);
+  const int chunk = to ^ ((ch >> 2) & 3) ^ ((ch >> 5) & 3);
+  return row * 64 + chunk * 16;
+}
+
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {  // (a.lo, b.lo)
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {  // (a.hi, b.hi)
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+__global__ void __launch_bounds__(SY_THREADS, 1)
+syrk_f16_mfma(const __half* __restrict__ X, int64_t n_tokens, int d, int64_t ldx, int nb, int ntiles,
+              int64_t tokens_per_split, float* __restrict__ partial) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][SY_T * SY_BK * 2];
+
+  const int tile = blockIdx.x % ntiles;
+  const int split = blockIdx.x / ntiles;
+  int bi, bj;
+  tile_coords(tile, nb, bi, bj);
+  const bool diag = (bi == bj);
+  const int I0 = bi * SY_T, J0 = bj * SY_T;
+  const int64_t kbeg = int64_t(split) * tokens_per_split;
+  int64_t kend = kbeg + tokens_per_split;
+  if (kend > n_tokens) kend = n_tokens;
+  const int nsteps = kend > kbeg ? int((kend - kbeg + SY_BK - 1) / SY_BK) : 0;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Loader role: panel p, channel octet c, token octet to.
+  const int lp = tid >> 7;
+  const int lu = tid & 127;
+  const int lc = lu & 31;
+  const int lto = lu >> 5;
+  const bool loader = !(diag && lp == 1);
+  const int lch0 = (lp == 0 ? I0 : J0) + 8 * lc;
+  const bool vec_ok = (lch0 + 8 <= d) && ((ldx & 7) == 0) &&
+                      ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
+
+  uint4 in[8];
+  auto gload = [&](int step) {
+    const int64_t t0 = kbeg + int64_t(step) * SY_BK + 8 * lto;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int64_t t = t0 + r;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (loader && t < kend) {
+        const __half* p = X + t * ldx + lch0;
+        if (vec_ok) {
+          v = *reinterpret_cast<const uint4*>(p);
+        } else {
+          unsigned short h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            h[e] = (lch0 + e < d) ? __half_as_ushort(p[e]) : (unsigned short)0;
+          v.x = h[0] | (uint32_t(h[1]) << 16);
+          v.y = h[2] | (uint32_t(h[3]) << 16);
+          v.z = h[4] | (uint32_t(h[5]) << 16);
+          v.w = h[6] | (uint32_t(h[7]) << 16);
+        }
+      }
+      in[r] = v;
+    }
+  };
+  auto lstore = [&](int stage) {
+    if (!loader) return;
+    unsigned char* base = lds[stage][lp];
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(in);
+    // in[r] word h = channels (2h, 2h+1) of token r.
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint4 o;
+        uint32_t* ow = reinterpret_cast<uint32_t*>(&o);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a = w[(2 * m) * 4 + h], c = w[(2 * m + 1) * 4 + h];
+          ow[m] = b ? hi_pair(a, c) : lo_pair(a, c);
+        }
+        const int ch = 8 * lc + 2 * h + b;
+        *reinterpret_cast<uint4*>(base + panel_off(ch, lto)) = o;
+      }
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
+
+  if (nsteps > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int st = s & 1;
+    if (s + 1 < nsteps) gload(s + 1);
+    const unsigned char* pa = lds[st][0];
+    const unsigned char* pb = diag ? lds[st][0] : lds[st][1];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int to = 2 * kk + (lane >> 5);
+      half8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = wm * 128 + i * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const half8*>(pa + panel_off(ch, to));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ch = wn * 128 + j * 32 + (lane & 31);
+        b[j] = *reinterpret_cast<const half8*>(pb + panel_off(ch, to));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < nsteps) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // Partial tile, row-major [256][256]. 32x32 MFMA result layout: lane l holds
+  // column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for register r.
+  float* out = partial + (int64_t(split) * ntiles + tile) * (SY_T * SY_T);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = wn * 128 + j * 32 + (lane & 31);
+        out[row * SY_T + col] = acc[i][j][r];
+      }
+}
+
+// fp32 inputs: VALU 64x64 tiles, 256 threads each holding a 4x4 block.
+__global__ void __launch_bounds__(256)
+syrk_f32_valu(const float* __restrict__ X, int64_t n_tokens, int d, int64_t ldx, int nb, int ntiles,
+              int64_t tokens_per_split, float* __restrict__ partial) {
+  __shared__ float sa[SYF_BK][SYF_T + 4];
+  __shared__ float sb[SYF_BK][SYF_T + 4];
+  const int tile = blockIdx.x % ntiles;
+  const int split = blockIdx.x / ntiles;
+  int bi, bj;
+  tile_coords(tile, nb, bi, bj);
+  const int I0 = bi * SYF_T, J0 = bj * SYF_T;
+  const int64_t kbeg = int64_t(split) * tokens_per_split;
+  int64_t kend = kbeg + tokens_per_split;
+  if (kend > n_tokens) kend = n_tokens;
+  const int tid = threadIdx.x;
+  const int ti = tid >> 4, tj = tid & 15;
+  float acc[4][4] = {};
+  for (int64_t k0 = kbeg; k0 < kend; k0 += SYF_BK) {
+    for (int e = tid; e < SYF_BK * SYF_T; e += 256) {
+      const int kk = e / SYF_T, c = e % SYF_T;
+      const int64_t t = k0 + kk;
+      sa[kk][c] = (t < kend && I0 + c < d) ? X[t * ldx + I0 + c] : 0.f;
+      sb[kk][c] = (t < kend && J0 + c < d) ? X[t * ldx + J0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < SYF_BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sa[kk][ti * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sb[kk][tj * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* out = partial + (int64_t(split) * ntiles + tile) * (SYF_T * SYF_T);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[(ti * 4 + i) * SYF_T + tj * 4 + j] = acc[i][j];
+}
+
+// H[i][j] = 2 * sum_s partial_s (min(i,j), max(i,j)) (+ H[i][j] if accumulate).
+// One 32x32 output block per workgroup; the source block (upper) is summed
+// into LDS in a fixed split order and written transposed where needed.
+__global__ void __launch_bounds__(256)
+syrk_reduce(const float* __restrict__ partial, int T, int nb, int ntiles, int nsplit, int d,
+            float* __restrict__ H, int accumulate) {
+  __shared__ double blk[32][33];
+  const int nob = (d + 31) / 32;
+  const int OI = blockIdx.x / nob, OJ = blockIdx.x % nob;
+  const int SI = OI < OJ ? OI : OJ, SJ = OI < OJ ? OJ : OI;  // source block, SI <= SJ
+  const int R0 = SI * 32, C0 = SJ * 32;
+  const int bi = R0 / T, bj = C0 / T;
+  const int tile = bi * nb - (bi * (bi - 1)) / 2 + (bj - bi);
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 32 * 32; e += 256) {
+    const int r = e >> 5, c = e & 31;
+    const int gr = R0 + r, gc = C0 + c;
+    double s = 0.0;
+    if (gr < d && gc < d) {
+      const int64_t off = int64_t(tile) * T * T + int64_t(gr - bi * T) * T + (gc - bj * T);
+      for (int sp = 0; sp < nsplit; ++sp) s += double(partial[int64_t(sp) * ntiles * T * T + off]);
+    }
+    blk[r][c] = s;
+  }
+  __syncthreads();
+  for (int e = tid; e < 32 * 32; e += 256) {
+    const int r = e >> 5, c = e & 31;
+    const int gi = OI * 32 + r, gj = OJ * 32 + c;
+    if (gi >= d || gj >= d) continue;
+    double v;
+    if (OI < OJ)
+      v = blk[r][c];
+    else if (OI > OJ)
+      v = blk[c][r];
+    else
+      v = r <= c ? blk[r][c] : blk[c][r];
+    v *= 2.0;
+    const int64_t o = int64_t(gi) * d + gj;
+    if (accumulate) v += double(H[o]);
+    H[o] = float(v);
+  }
+}
+
+__global__ void fill_zero_f32(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0.f;
+}
+
+struct SyrkPlan {
+  int T, nb, ntiles, nsplit;
+  int64_t tokens_per_split;
+  size_t ws_bytes;
+};
+
+SyrkPlan plan_syrk(int64_t n_tokens, int64_t d, int xdtype) {
+  SyrkPlan p{};
+  const int bk = xdtype == GPTQ_F16 ? SY_BK : SYF_BK;
+  p.T = xdtype == GPTQ_F16 ? SY_T : SYF_T;
+  p.nb = int((d + p.T - 1) / p.T);
+  p.ntiles = p.nb * (p.nb + 1) / 2;
+  const int64_t ksteps = (n_tokens + bk - 1) / bk;
+  // Enough workgroups to keep 256 CUs busy for several rounds, at least 4
+  // partial sums for accuracy, never more splits than token steps.
+  int64_t want = (2048 + p.ntiles - 1) / p.ntiles;
+  if (want < 4) want = 4;
+  if (want > ksteps) want = ksteps;
+  if (want < 1) want = 1;
+  p.tokens_per_split = ((ksteps + want - 1) / want) * bk;
+  p.nsplit = n_tokens > 0 ? int((n_tokens + p.tokens_per_split - 1) / p.tokens_per_split) : 0;
+  p.ws_bytes = align_up(size_t(p.nsplit) * p.ntiles * p.T * p.T * sizeof(float), 256);
+  return p;
+}
+
+}  // namespace
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_hessian_workspace_size(int64_t n_tokens, int64_t d, int xdtype) {
+  if (d < 1 || n_tokens < 0 || (xdtype != GPTQ_F16 && xdtype != GPTQ_F32)) return 0;
+  return plan_syrk(n_tokens, d, xdtype).ws_bytes;
+}
+
+extern "C" int gptq_hessian_accumulate(const void* X, int xdtype, int64_t n_tokens, int64_t d, int64_t ldx,
+                                       float* H, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  if (d < 1 || d > (1 << 20) || n_tokens < 0 || ldx < d || H == nullptr) return GPTQ_E_INVALID_ARG;
+  if (xdtype != GPTQ_F16 && xdtype != GPTQ_F32) return GPTQ_E_INVALID_ARG;
+  if (n_tokens > 0 && X == nullptr) return GPTQ_E_INVALID_ARG;
+  hipStream_t s = as_stream(stream);
+  if (n_tokens == 0) {
+    if (!accumulate) {
+      hipLaunchKernelGGL(fill_zero_f32, dim3(1024), dim3(256), 0, s, H, d * d);
+      return launch_status();
+    }
+    return GPTQ_OK;
+  }
+  const SyrkPlan p = plan_syrk(n_tokens, d, xdtype);
+  if (ws == nullptr || ws_bytes < p.ws_bytes) return GPTQ_E_WORKSPACE;
+  float* partial = static_cast<float*>(ws);
+  const dim3 grid(unsigned(int64_t(p.ntiles) * p.nsplit));
+  if (xdtype == GPTQ_F16) {
+    hipLaunchKernelGGL(syrk_f16_mfma, grid, dim3(SY_THREADS), 0, s, static_cast<const __half*>(X), n_tokens,
+                       int(d), ldx, p.nb, p.ntiles, p.tokens_per_split, partial);
+  } else {
+    hipLaunchKernelGGL(syrk_f32_valu, grid, dim3(256), 0, s, static_cast<const float*>(X), n_tokens, int(d), ldx,
+                       p.nb, p.ntiles, p.tokens_per_split, partial);
+  }
+  if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+  const int nob = int((d + 31) / 32);
+  hipLaunchKernelGGL(syrk_reduce, dim3(unsigned(nob * nob)), dim3(256), 0, s, partial, p.T, p.nb, p.ntiles,
+                     p.nsplit, int(d), H, accumulate);
+  return launch_status();
+}

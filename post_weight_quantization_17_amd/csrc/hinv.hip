@@ -1,0 +1,346 @@
+// Stage 2 of the GPTQ layer path: U, the upper Cholesky factor of
+// (H + lambda I)^-1, lambda = damp * mean(diag H).
+//
+// astro-blog LLM quantization survey, section 2.3 item 3, and the xuzou.cn
+// reading card of the GPTQ paper, section 方法适配: the sweep's inverse
+// Hessian rows are precomputed with a Cholesky factorization of the mildly
+// damped Hessian, which the pages describe as more robust than updating an
+// explicit inverse.
+//
+// Route taken here (same U, half the flops of "invert, then factor"):
+// let J be the index reversal and A = J H_d J. With A = L L^T (L lower),
+// H_d = V V^T for the upper V = J L J, and H_d^-1 = U^T U with U = V^-1 =
+// J L^-1 J. The Cholesky factor with positive diagonal is unique, so this is
+// the factor of H_d^-1 itself.
+//
+// L and X = L^-1 are computed together by a right-looking blocked
+// elimination in fp64 (panel width 64):
+//   diag   (1 workgroup): L_kk = chol(A_kk) and X_kk = L_kk^-1 in LDS; a
+//          pivot that is not positive sets `info`.
+//   panel  (many):        L_ik = A_ik X_kk^T            for row blocks i > k
+//                         X[k, :k] = X_kk R[k, :k]      (block row k of X)
+//   update (many):        A_ij -= L_ik L_jk^T           (trailing lower part)
+//                         R[i, :k+1] -= L_ik X[k, :k+1] (rows i > k)
+// R starts as the identity; block row i of R becomes block row i of X once
+// its own panel step runs. Each step's products are 64x64 tiles on the fp64
+// MFMA (v_mfma_f64_16x16x4f64).
+#include "gptq_common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int NB = 64;   // panel width
+constexpr int LP = 68;   // LDS pitch (doubles) of 64-wide operand tiles
+
+// ---------------------------------------------------------------- setup
+__global__ void __launch_bounds__(256)
+hinv_lambda(const float* __restrict__ H, int d, double damp, double* __restrict__ lam,
+            float* __restrict__ lambda_out, int32_t* __restrict__ info) {
+  __shared__ double part[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < d; i += 256) s += double(H[int64_t(i) * d + i]);
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double l = damp * (part[0] / double(d));
+    *lam = l;
+    if (lambda_out) *lambda_out = float(l);
+    *info = 0;
+  }
+}
+
+// A[i][j] = H[d-1-j][d-1-i] + lambda [i == j] for j <= i (reads H's lower
+// triangle, which is the reversed matrix's lower triangle by symmetry);
+// R = identity on and below the diagonal. One 32x32 lower block per group.
+__global__ void __launch_bounds__(256)
+hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, double* __restrict__ A,
+           double* __restrict__ R) {
+  __shared__ float t[32][33];
+  int b = blockIdx.x, bi = 0;
+  while (b > bi) {
+    b -= bi + 1;
+    ++bi;
+  }
+  const int bj = b;  // bj <= bi
+  const int i0 = bi * 32, j0 = bj * 32;
+  const double l = *lam;
+  for (int e = threadIdx.x; e < 1024; e += 256) {
+    const int jj = e >> 5, ii = e & 31;
+    const int i = i0 + ii, j = j0 + jj;
+    t[jj][ii] = (i < d && j < d) ? H[int64_t(d - 1 - j) * d + (d - 1 - i)] : 0.f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 1024; e += 256) {
+    const int ii = e >> 5, jj = e & 31;
+    const int i = i0 + ii, j = j0 + jj;
+    if (i >= d || j >= d || j > i) continue;
+    const int64_t o = int64_t(i) * d + j;
+    A[o] = double(t[jj][ii]) + (i == j ? l : 0.0);
+    R[o] = (i == j) ? 1.0 : 0.0;
+  }
+}
+
+// ------------------------------------------------------------ diag block
+// Factor the kb x kb diagonal block at k0 and invert its factor. Schur form:
+// step j eliminates column j with multipliers m_i = a_ij / a_jj, applied both
+// to the trailing block (a_ic -= m_i a_cj, c in (j, i]) and to the unit-lower
+// inverse Y (y_ic -= m_i y_jc, c <= j). Then L_ij = a_ij / sqrt(a_jj) and
+// L^-1_ic = y_ic / sqrt(a_ii).
+__global__ void __launch_bounds__(256)
+hinv_diag(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, double* __restrict__ Lbuf,
+          int32_t* __restrict__ info) {
+  __shared__ double a[NB][NB + 1];
+  __shared__ double y[NB][NB + 1];
+  __shared__ double sq[NB];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int i = e / NB, c = e % NB;
+    double v = 0.0;
+    if (i < kb && c <= i) v = A[int64_t(k0 + i) * d + k0 + c];
+    a[i][c] = v;
+    y[i][c] = (i == c) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int j = 0; j < kb; ++j) {
+    const double piv = a[j][j];
+    if (tid == 0 && !(piv > 0.0)) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + j)));
+    const double inv = 1.0 / piv;
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int i = e / NB, c = e % NB;
+      if (i <= j || i >= kb || c > i) continue;
+      const double m = a[i][j] * inv;
+      if (c > j)
+        a[i][c] -= m * a[c][j];
+      else
+        y[i][c] -= m * y[j][c];
+    }
+    __syncthreads();
+  }
+  if (tid < kb) sq[tid] = sqrt(a[tid][tid]);
+  __syncthreads();
+  for (int e = tid; e < NB * NB; e += 256) {
+    const int i = e / NB, c = e % NB;
+    double l = 0.0, x = 0.0;
+    if (i < kb && c <= i) {
+      l = (c == i) ? sq[i] : a[i][c] / sq[c];
+      x = y[i][c] / sq[i];
+      A[int64_t(k0 + i) * d + k0 + c] = l;
+      R[int64_t(k0 + i) * d + k0 + c] = x;
+    }
+    Lbuf[i * NB + c] = x;  // X_kk, zero outside the kb x kb lower triangle
+  }
+}
+
+// ------------------------------------------------------ 64x64 tile products
+// Each of the 4 waves owns a 32x32 quarter (2x2 MFMA 16x16 blocks).
+// Ls[i][k] (pitch LP) is the left operand, Rs[k][j] (pitch LP) the right one;
+// K is a multiple of 4 (zero padded).
+__device__ __forceinline__ void tile_mma(const double (*Ls)[LP], const double (*Rs)[LP], int K, doublex4 acc[2][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  for (int k = 0; k < K; k += 4) {
+    double av[2], bv[2];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) av[ii] = Ls[wr * 32 + ii * 16 + (lane & 15)][k + (lane >> 4)];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) bv[jj] = Rs[k + (lane >> 4)][wc * 32 + jj * 16 + (lane & 15)];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        acc[ii][jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii], bv[jj], acc[ii][jj], 0, 0, 0);
+  }
+}
+
+// Visit the wave's accumulator elements: f(row, col, value) in tile coords.
+// v_mfma_f64_16x16x4f64 result layout: lane l, register r holds row
+// (l / 16) + 4 r, column l % 16 of the 16x16 block.
+template <typename F>
+__device__ __forceinline__ void tile_for_each(doublex4 acc[2][2], F f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        f(wr * 32 + ii * 16 + (lane >> 4) + 4 * r, wc * 32 + jj * 16 + (lane & 15), acc[ii][jj][r]);
+}
+
+// ------------------------------------------------------------ panel step
+// Blocks [0, nrow): L_ik for row block i = k1 + 64 b (in place in A).
+// Blocks [nrow, nrow + ncol): X[k, c0:c0+64] = X_kk R[k, c0:c0+64], c0 < k0
+// (in place in R).
+__global__ void __launch_bounds__(256)
+hinv_panel(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, const double* __restrict__ Lbuf,
+           int nrow) {
+  __shared__ double Ls[NB][LP];
+  __shared__ double Rs[NB][LP];
+  const int tid = threadIdx.x;
+  const int k1 = k0 + kb;
+  const int Kp = (kb + 3) & ~3;
+  doublex4 acc[2][2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
+  if (int(blockIdx.x) < nrow) {
+    const int r0 = k1 + NB * blockIdx.x;
+    // left: A[r0+i][k0+m]; right[m][j] = X_kk[j][m]
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int i = e / NB, m = e % NB;
+      Ls[i][m] = (r0 + i < d && m < kb) ? A[int64_t(r0 + i) * d + k0 + m] : 0.0;
+      Rs[m][i] = Lbuf[i * NB + m];
+    }
+    __syncthreads();
+    tile_mma(Ls, Rs, Kp, acc);
+    tile_for_each(acc, [&](int i, int j, double v) {
+      if (r0 + i < d && j < kb) A[int64_t(r0 + i) * d + k0 + j] = v;
+    });
+  } else {
+    const int c0 = NB * (blockIdx.x - nrow);
+    // left: X_kk[i][m]; right[m][c] = R[k0+m][c0+c]
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int i = e / NB, c = e % NB;
+      Ls[i][c] = Lbuf[i * NB + c];
+      Rs[i][c] = (i < kb && c0 + c < k0) ? R[int64_t(k0 + i) * d + c0 + c] : 0.0;
+    }
+    __syncthreads();
+    tile_mma(Ls, Rs, Kp, acc);
+    tile_for_each(acc, [&](int i, int c, double v) {
+      if (i < kb && c0 + c < k0) R[int64_t(k0 + i) * d + c0 + c] = v;
+    });
+  }
+}
+
+// ----------------------------------------------------------- update step
+// Blocks [0, nA): lower tiles (ti >= tj) of the trailing matrix at k1:
+//   A_ij -= L_i L_j^T.
+// Blocks [nA, nA + nT * nC): R[k1 + 64 ti, 64 tc] -= L_i X[k, 64 tc].
+__global__ void __launch_bounds__(256)
+hinv_update(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, int nT, int nC) {
+  __shared__ double Ls[NB][LP];
+  __shared__ double Rs[NB][LP];
+  const int tid = threadIdx.x;
+  const int k1 = k0 + kb;
+  const int Kp = (kb + 3) & ~3;
+  const int nA = nT * (nT + 1) / 2;
+  int b = blockIdx.x;
+  doublex4 acc[2][2];
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
+  if (b < nA) {
+    int ti = 0;
+    while (b > ti) {
+      b -= ti + 1;
+      ++ti;
+    }
+    const int tj = b;
+    const int r0 = k1 + NB * ti, c0 = k1 + NB * tj;
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int i = e / NB, m = e % NB;
+      Ls[i][m] = (r0 + i < d && m < kb) ? A[int64_t(r0 + i) * d + k0 + m] : 0.0;
+      Rs[m][i] = (c0 + i < d && m < kb) ? A[int64_t(c0 + i) * d + k0 + m] : 0.0;
+    }
+    __syncthreads();
+    tile_mma(Ls, Rs, Kp, acc);
+    tile_for_each(acc, [&](int i, int j, double v) {
+      if (r0 + i < d && c0 + j < d && c0 + j <= r0 + i) A[int64_t(r0 + i) * d + c0 + j] -= v;
+    });
+  } else {
+    b -= nA;
+    const int ti = b / nC, tc = b % nC;
+    const int r0 = k1 + NB * ti, c0 = NB * tc;
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int i = e / NB, m = e % NB;
+      Ls[i][m] = (r0 + i < d && m < kb) ? A[int64_t(r0 + i) * d + k0 + m] : 0.0;
+    }
+    for (int e = tid; e < NB * NB; e += 256) {
+      const int m = e / NB, c = e % NB;
+      // X[k, :k1] is block row k of X: lower triangular inside the diagonal
+      // block (R's upper part is never written, so it is masked here).
+      Rs[m][c] = (m < kb && c0 + c < k1 && c0 + c <= k0 + m) ? R[int64_t(k0 + m) * d + c0 + c] : 0.0;
+    }
+    __syncthreads();
+    tile_mma(Ls, Rs, Kp, acc);
+    tile_for_each(acc, [&](int i, int c, double v) {
+      if (r0 + i < d && c0 + c < k1) R[int64_t(r0 + i) * d + c0 + c] -= v;
+    });
+  }
+}
+
+// U[i][j] = X[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
+__global__ void __launch_bounds__(256)
+hinv_write_u(const double* __restrict__ R, int d, float* __restrict__ U) {
+  const int64_t n = int64_t(d) * d;
+  for (int64_t e = blockIdx.x * int64_t(256) + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256) {
+    const int i = int(e / d), j = int(e % d);
+    U[e] = (i <= j) ? float(R[int64_t(d - 1 - i) * d + (d - 1 - j)]) : 0.f;
+  }
+}
+
+struct HinvWs {
+  double *A, *R, *lam, *Lbuf;
+  size_t bytes;
+};
+
+HinvWs carve(void* ws, int64_t d) {
+  HinvWs w{};
+  const size_t mat = align_up(size_t(d) * d * sizeof(double), 256);
+  char* p = static_cast<char*>(ws);
+  w.A = reinterpret_cast<double*>(p);
+  w.R = reinterpret_cast<double*>(p + mat);
+  w.lam = reinterpret_cast<double*>(p + 2 * mat);
+  w.Lbuf = reinterpret_cast<double*>(p + 2 * mat + 256);
+  w.bytes = 2 * mat + 256 + align_up(NB * NB * sizeof(double), 256);
+  return w;
+}
+
+}  // namespace
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_prepare_hinv_workspace_size(int64_t d) {
+  if (d < 1) return 0;
+  return carve(nullptr, d).bytes;
+}
+
+extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* lambda_out, int32_t* info,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  if (d < 1 || d > 65536 || H == nullptr || U == nullptr || info == nullptr) return GPTQ_E_INVALID_ARG;
+  if (!(damp >= 0.0) || damp > 1e30) return GPTQ_E_INVALID_ARG;
+  const HinvWs w = carve(ws, d);
+  if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_E_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  const int di = int(d);
+  hipLaunchKernelGGL(hinv_lambda, dim3(1), dim3(256), 0, s, H, di, damp, w.lam, lambda_out, info);
+  const int nb32 = (di + 31) / 32;
+  hipLaunchKernelGGL(hinv_setup, dim3(unsigned(nb32 * (nb32 + 1) / 2)), dim3(256), 0, s, H, di, w.lam, w.A, w.R);
+  if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+  for (int k0 = 0; k0 < di; k0 += NB) {
+    const int kb = di - k0 < NB ? di - k0 : NB;
+    const int k1 = k0 + kb;
+    hipLaunchKernelGGL(hinv_diag, dim3(1), dim3(256), 0, s, w.A, w.R, di, k0, kb, w.Lbuf, info);
+    const int nrow = (di - k1 + NB - 1) / NB;
+    const int ncol = (k0 + NB - 1) / NB;
+    if (nrow + ncol > 0)
+      hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, di, k0, kb, w.Lbuf,
+                         nrow);
+    const int nT = nrow;
+    const int nC = (k1 + NB - 1) / NB;
+    const int nblk = nT * (nT + 1) / 2 + nT * nC;
+    if (nblk > 0)
+      hipLaunchKernelGGL(hinv_update, dim3(unsigned(nblk)), dim3(256), 0, s, w.A, w.R, di, k0, kb, nT, nC);
+    if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+  }
+  hipLaunchKernelGGL(hinv_write_u, dim3(2048), dim3(256), 0, s, w.R, di, U);
+  return launch_status();
+}

@@ -1,0 +1,411 @@
+// Stage 3 of the GPTQ layer path: the fixed-order column sweep.
+//
+// What is computed (aiqz.cc "GPTQ：一键量化大模型压缩", sections 误差补偿 and
+// 分组方案; astro-blog LLM quantization survey, sections 1.2, 2.2, 2.3;
+// xuzou.cn reading card of the GPTQ paper, section 方法适配): every row is
+// swept over its columns in natural order; column q is rounded on its group's
+// min-max grid, and its error, divided by U_qq, is spread over the row's
+// later columns through row q of U (the upper Cholesky factor of H_d^-1).
+// Blocks of 128 columns defer the update of all later columns to the end of
+// the block, where it is one rank-128 product.
+//
+// Design (gfx950): rows are independent given U, so one persistent
+// workgroup owns 16 rows for the whole sweep and needs no grid-wide
+// synchronization. Per 128-column block it
+//   1. stages U[blk, blk] (64 KB fp32) and 1/U_qq in LDS;
+//   2. runs the 128 sequential column steps with each row spread over one
+//      16-lane DPP row (8 columns per lane, interleaved): the current value
+//      of column q is broadcast from its owner lane with DPP row_newbcast,
+//      every lane of the row takes the same rounding decision, and each lane
+//      applies the rank-1 update to its own columns (U row q from LDS);
+//   3. writes codes, packs the block's 32-bit words from an LDS copy of the
+//      codes (128 * bits is a whole number of words), and stores the errors
+//      e = err / U_qq in LDS;
+//   4. applies W[rows, i2:] -= E U[blk, i2:] with v_mfma_f32_16x16x4f32 (the
+//      workgroup's 16 rows are exactly one MFMA M tile; each lane's 4
+//      consecutive output columns make W and U accesses 16-byte vectors),
+//      in an fp32 working copy of W in the workspace.
+// The first block reads the caller's W directly (no conversion pass).
+// Group statistics for a group that starts at column q are taken from the
+// current values when the sweep reaches q. The loss sum is kept in fp64.
+#include <utility>
+
+#include "gptq_common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int QB = 128;        // block width
+constexpr int QR = 16;         // rows per workgroup
+constexpr int QT = 256;        // threads per workgroup
+constexpr int QM = QB / 16;    // columns per lane per block
+
+template <int Q, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (Q < N) {
+    f(std::integral_constant<int, Q>{});
+    static_for<Q + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(__half v) { return __half2float(v); }
+
+__device__ __forceinline__ floatx4 load4(const float* p) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  return floatx4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ floatx4 load4(const __half* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  const __half2 a = *reinterpret_cast<const __half2*>(&v.x);
+  const __half2 b = *reinterpret_cast<const __half2*>(&v.y);
+  return floatx4{__low2float(a), __high2float(a), __low2float(b), __high2float(b)};
+}
+
+// Min-max grid of one group: the range always includes 0; an all-zero group
+// uses [-1, 1]. s = (xmax - xmin)/maxq, z = rint(-xmin/s).
+__device__ __forceinline__ void grid_params(float mn, float mx, float maxq, float& s, float& z, float& rs) {
+  if (mn == 0.f && mx == 0.f) {
+    mn = -1.f;
+    mx = 1.f;
+  }
+  s = (mx - mn) / maxq;
+  z = rintf(-mn / s);
+  rs = 1.f / s;
+}
+
+// x / s rounded to nearest fp32 from rs = RN(1/s): q = RN(x rs) is within an
+// ulp of x/s, the residual x - q s is exact in one fma, and one correction
+// step q + (x - q s) rs gives the correctly rounded quotient (Markstein's
+// division theorem), i.e. the same value as an IEEE division, in 3 ops.
+__device__ __forceinline__ float div_rn(float x, float s, float rs) {
+  const float q = x * rs;
+  const float r = fmaf(-q, s, x);
+  return fmaf(r, rs, q);
+}
+
+template <typename WT>
+__global__ void __launch_bounds__(QT, 2)
+gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __restrict__ U, int d_row, int d_col,
+           int bits, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
+           int32_t* __restrict__ zeros, uint32_t* __restrict__ packed, int nwords, float* __restrict__ row_loss,
+           double* __restrict__ wg_loss) {
+  __shared__ __attribute__((aligned(16))) float Ud[QB][QB];
+  __shared__ float dinv[QB];
+  __shared__ float Es[QR][QB + 4];
+  __shared__ uint8_t Cs[QR][QB];
+  __shared__ double Lsum[QR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rloc = wave * 4 + (lane >> 4);
+  const int sub = lane & 15;
+  const int row0 = blockIdx.x * QR;
+  const int row = row0 + rloc;
+  const bool row_ok = row < d_row;
+  const size_t rbase = size_t(row) * d_col;
+  const float maxq = float((1 << bits) - 1);
+
+  float s = 1.f, z = 0.f, rs = 1.f;
+  double lacc = 0.0;
+
+  if (group < 0) {  // one group per row, from the original row
+    float mn = 0.f, mx = 0.f;
+    if (row_ok)
+      for (int j = sub; j < d_col; j += 16) {
+        const float v = to_f(W[rbase + j]);
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+    mn = row16_min(mn);
+    mx = row16_max(mx);
+    grid_params(mn, mx, maxq, s, z, rs);
+    if (sub == 0 && row_ok) {
+      scales[row] = s;
+      zeros[row] = int(z);
+    }
+  }
+
+  for (int i1 = 0; i1 < d_col; i1 += QB) {
+    const int nvalid = d_col - i1 < QB ? d_col - i1 : QB;
+    const bool first = (i1 == 0);
+
+    // 1. U block (upper part; padded columns act as identity rows) and W block.
+    for (int e = tid; e < QB * QB; e += QT) {
+      const int k = e >> 7, j = e & (QB - 1);
+      float v;
+      if (k < nvalid && j < nvalid)
+        v = j >= k ? U[size_t(i1 + k) * d_col + i1 + j] : 0.f;
+      else
+        v = (k == j) ? 1.f : 0.f;
+      Ud[k][j] = v;
+    }
+    float wr[QM], cr[QM], er[QM];
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+      const int jl = 16 * m + sub;
+      float v = 0.f;
+      if (row_ok && jl < nvalid) v = first ? to_f(W[rbase + i1 + jl]) : Wf[rbase + i1 + jl];
+      wr[m] = v;
+      cr[m] = 0.f;
+      er[m] = 0.f;
+    }
+    __syncthreads();
+    if (tid < QB) dinv[tid] = 1.f / Ud[tid][tid];
+    __syncthreads();
+
+    // 2. The 128 sequential column steps.
+    static_for<0, QB>([&](auto qc) {
+      constexpr int q = decltype(qc)::value;
+      constexpr int m = q / 16;
+      constexpr int o = q % 16;
+      if constexpr (o == 0) {
+        if (group > 0 && q < nvalid && (i1 + q) % group == 0) {
+          float mn = 0.f, mx = 0.f;
+#pragma unroll
+          for (int mm = m; mm < QM; ++mm) {
+            const float v = (16 * mm + sub < q + group) ? wr[mm] : 0.f;
+            mn = fminf(mn, v);
+            mx = fmaxf(mx, v);
+          }
+          if (group > QB) {
+            const int jend = i1 + group < d_col ? i1 + group : d_col;
+            if (row_ok)
+              for (int j = i1 + QB + sub; j < jend; j += 16) {
+                const float v = first ? to_f(W[rbase + j]) : Wf[rbase + j];
+                mn = fminf(mn, v);
+                mx = fmaxf(mx, v);
+              }
+          }
+          mn = row16_min(mn);
+          mx = row16_max(mx);
+          grid_params(mn, mx, maxq, s, z, rs);
+          if (sub == 0 && row_ok) {
+            const int g = (i1 + q) / group;
+            scales[size_t(row) * ngroups + g] = s;
+            zeros[size_t(row) * ngroups + g] = int(z);
+          }
+        }
+      }
+      const float x = row_bcast<o>(wr[m]);
+      float c = rintf(div_rn(x, s, rs)) + z;
+      c = fminf(fmaxf(c, 0.f), maxq);
+      const float what = s * (c - z);
+      const float err = x - what;
+      const float e = err * dinv[q];
+      lacc = fma(0.5 * double(e), double(e), lacc);
+      // Keep the owner's code and error as they are produced (otherwise the
+      // compiler defers the selects and keeps all 16 steps' values live).
+      cr[m] = sub == o ? c : cr[m];
+      er[m] = sub == o ? e : er[m];
+      asm volatile("" : "+v"(cr[m]), "+v"(er[m]), "+v"(lacc));
+#pragma unroll
+      for (int mm = m; mm < QM; ++mm) wr[mm] = fmaf(-e, Ud[q][16 * mm + sub], wr[mm]);
+    });
+
+    // 3. Codes, packed words, errors.
+#pragma unroll
+    for (int m = 0; m < QM; ++m) {
+      const int jl = 16 * m + sub;
+      const uint8_t cv = uint8_t(cr[m]);
+      if (row_ok && jl < nvalid) codes[rbase + i1 + jl] = cv;
+      Cs[rloc][jl] = cv;
+      Es[rloc][jl] = er[m];
+    }
+    __syncthreads();
+    {
+      const int nwb = (nvalid * bits + 31) / 32;
+      const int wbase = (i1 * bits) / 32;
+      if (row_ok)
+        for (int w = sub; w < nwb; w += 16)
+          packed[size_t(row) * nwords + wbase + w] = pack_word(Cs[rloc], nvalid, bits, w);
+    }
+
+    // 4. Deferred update of the later columns: W[:, i2:] -= E U[blk, i2:].
+    const int i2 = i1 + QB;
+    if (i2 < d_col) {
+      const int li = lane & 15, lk = lane >> 4;
+      for (int n0 = i2 + 64 * wave; n0 < d_col; n0 += 256) {
+        const int col = n0 + 4 * li;
+        const bool full = vec4 && (n0 + 64 <= d_col);
+        floatx4 acc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = row0 + 4 * lk + r;
+          floatx4 v = {0.f, 0.f, 0.f, 0.f};
+          if (rr < d_row) {
+            const size_t off = size_t(rr) * d_col + col;
+            if (full) {
+              v = first ? load4(W + off) : load4(Wf + off);
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                if (col + t < d_col) v[t] = first ? to_f(W[off + t]) : Wf[off + t];
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[t][r] = v[t];
+        }
+#pragma unroll 8
+        for (int t = 0; t < QB / 4; ++t) {
+          const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
+          const size_t uoff = size_t(i1 + 4 * t + lk) * d_col + col;
+          floatx4 b = {0.f, 0.f, 0.f, 0.f};
+          if (full) {
+            b = load4(U + uoff);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (col + u < d_col) b[u] = U[uoff + u];
+          }
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[v], 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = row0 + 4 * lk + r;
+          if (rr >= d_row) continue;
+          const size_t off = size_t(rr) * d_col + col;
+          if (full) {
+            *reinterpret_cast<float4*>(Wf + off) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              if (col + t < d_col) Wf[off + t] = acc[t][r];
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (sub == 0) {
+    Lsum[rloc] = row_ok ? lacc : 0.0;
+    if (row_ok && row_loss) row_loss[row] = float(lacc);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int r = 0; r < QR; ++r) t += Lsum[r];
+    wg_loss[blockIdx.x] = t;
+  }
+}
+
+// Sum of the per-workgroup losses in a fixed order.
+__global__ void __launch_bounds__(256) loss_final(const double* __restrict__ part, int n, double* __restrict__ loss) {
+  __shared__ double sh[256];
+  double t = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) t += part[i];
+  sh[threadIdx.x] = t;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) sh[threadIdx.x] += sh[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = sh[0];
+}
+
+__global__ void __launch_bounds__(256)
+pack_codes_kernel(const uint8_t* __restrict__ codes, int64_t d_row, int d_col, int bits, uint32_t* __restrict__ packed,
+                  int nwords) {
+  const int64_t n = d_row * nwords;
+  for (int64_t i = blockIdx.x * int64_t(256) + threadIdx.x; i < n; i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / nwords;
+    const int w = int(i % nwords);
+    packed[i] = pack_word(codes + r * d_col, d_col, bits, w);
+  }
+}
+
+inline bool bits_ok(int b) { return b == 2 || b == 3 || b == 4 || b == 8; }
+
+struct QuantWs {
+  float* Wf;
+  double* wg_loss;
+  size_t bytes;
+};
+
+QuantWs carve_q(void* ws, int64_t d_row, int64_t d_col) {
+  QuantWs w{};
+  const size_t wf = align_up(size_t(d_row) * d_col * sizeof(float), 256);
+  const int64_t nwg = (d_row + QR - 1) / QR;
+  char* p = static_cast<char*>(ws);
+  w.Wf = reinterpret_cast<float*>(p);
+  w.wg_loss = reinterpret_cast<double*>(p + wf);
+  w.bytes = wf + align_up(size_t(nwg) * sizeof(double), 256);
+  return w;
+}
+
+}  // namespace
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int bits, int64_t group_size,
+                                                     int64_t block) {
+  (void)bits;
+  (void)group_size;
+  (void)block;
+  if (d_row < 1 || d_col < 1) return 0;
+  return carve_q(nullptr, d_row, d_col).bytes;
+}
+
+extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U, int bits,
+                                   int64_t group_size, int64_t block, uint8_t* codes, float* scales, int32_t* zeros,
+                                   uint32_t* packed, double* loss, float* row_loss, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  if (d_row < 1 || d_col < 1 || d_row > (int64_t(1) << 30) || d_col > (1 << 20)) return GPTQ_E_INVALID_ARG;
+  if (d_row * d_col > (int64_t(1) << 40)) return GPTQ_E_INVALID_ARG;
+  if (!W || !U || !codes || !scales || !zeros || !packed || !loss) return GPTQ_E_INVALID_ARG;
+  if (wdtype != GPTQ_F16 && wdtype != GPTQ_F32) return GPTQ_E_INVALID_ARG;
+  if (!bits_ok(bits)) return GPTQ_E_INVALID_ARG;
+  if (block < 1) return GPTQ_E_INVALID_ARG;
+  if (group_size != -1) {
+    if (group_size < 1 || (block % group_size != 0 && group_size % block != 0)) return GPTQ_E_INVALID_ARG;
+  }
+  if (block != QB) return GPTQ_E_UNSUPPORTED;
+  if (group_size != -1 && group_size % 16 != 0) return GPTQ_E_UNSUPPORTED;
+  const QuantWs w = carve_q(ws, d_row, d_col);
+  if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_E_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  const int ngroups = group_size == -1 ? 1 : int((d_col + group_size - 1) / group_size);
+  const int nwords = int((d_col * bits + 31) / 32);
+  const unsigned nwg = unsigned((d_row + QR - 1) / QR);
+  const int esz = wdtype == GPTQ_F16 ? 2 : 4;
+  const int vec4 = (d_col % 4 == 0) && (reinterpret_cast<uintptr_t>(W) % (4 * esz) == 0) &&
+                   (reinterpret_cast<uintptr_t>(U) % 16 == 0) ? 1 : 0;
+  if (wdtype == GPTQ_F16)
+    hipLaunchKernelGGL(gptq_sweep<__half>, dim3(nwg), dim3(QT), 0, s, static_cast<const __half*>(W), w.Wf, U,
+                       int(d_row), int(d_col), bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed,
+                       nwords, row_loss, w.wg_loss);
+  else
+    hipLaunchKernelGGL(gptq_sweep<float>, dim3(nwg), dim3(QT), 0, s, static_cast<const float*>(W), w.Wf, U,
+                       int(d_row), int(d_col), bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed,
+                       nwords, row_loss, w.wg_loss);
+  if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+  hipLaunchKernelGGL(loss_final, dim3(1), dim3(256), 0, s, w.wg_loss, int(nwg), loss);
+  return launch_status();
+}
+
+extern "C" int gptq_pack_codes(const uint8_t* codes, int64_t d_row, int64_t d_col, int bits, uint32_t* packed,
+                               void* stream) {
+  if (d_row < 1 || d_col < 1 || d_col > (1 << 24) || !codes || !packed || !bits_ok(bits)) return GPTQ_E_INVALID_ARG;
+  const int nwords = int((d_col * bits + 31) / 32);
+  const int64_t n = d_row * nwords;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_codes_kernel, dim3(unsigned(blocks)), dim3(256), 0, as_stream(stream), codes, d_row,
+                     int(d_col), bits, packed, nwords);
+  return launch_status();
+}
+
+extern "C" const char* gptq_status_string(int status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_E_INVALID_ARG: return "invalid argument";
+    case GPTQ_E_UNSUPPORTED: return "unsupported parameter";
+    case GPTQ_E_WORKSPACE: return "workspace too small";
+    case GPTQ_E_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" const char* gptq_version(void) { return "0.1.0"; }
