@@ -110,6 +110,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="attn_proj_4096x4096_4bit_g128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument(
+        "--copy-calibration",
+        action="store_true",
+        help="only run a plain 1 GiB device-to-device copy (3 times), the reference for HBM byte counters",
+    )
     args = ap.parse_args()
     if args.gpus != 1:
         print(
@@ -120,6 +125,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_copy": 1 << 30, "bytes_written_per_copy": 1 << 30}))
+        return
 
     import post_weight_quantization_17_amd as g
     from workload import CONFIGS, weights

@@ -9,12 +9,14 @@
 //  * Only upper 256x256 tiles (bi <= bj) are computed. Each workgroup
 //    (4 waves, 2x2, each wave 128x128 = 4x4 MFMA 32x32x16 f16 tiles) owns one
 //    tile for one contiguous token range (split-K).
-//  * X tiles are read from HBM with 16-byte loads along channels (8 tokens
-//    x 8 channels per thread), transposed in registers with v_perm so each
-//    channel's 8 consecutive tokens form one 16-byte LDS chunk, and stored in
-//    a swizzled [channel][32 tokens] LDS layout. MFMA operands for both sides
-//    are then single ds_read_b128 per lane. Two LDS stages double-buffer the
-//    token loop; global loads of step k+1 overlap the MFMAs of step k.
+//  * X is copied from HBM straight into LDS (global_load_lds, 16 bytes per
+//    lane) in its natural token-major layout, double buffered so the loads of
+//    step k+1 overlap the MFMAs of step k; no registers or VALU work are
+//    spent on staging. MFMA operands need 8 consecutive tokens of one channel
+//    per lane: they are read with the gfx950 transposing LDS read
+//    (ds_read_b64_tr_b16), two per fragment, at per-lane base + immediate
+//    offsets. Ragged tokens or channels take a checked register path into
+//    the same layout.
 //  * fp16 products are exact in fp32 and MFMA accumulates in fp32. Each
 //    split writes its partial tile to the workspace; a second kernel sums the
 //    splits in a fixed order in fp64, scales by 2, mirrors the upper tiles
@@ -43,6 +45,10 @@ __device__ __forceinline__ void tile_coords(int tile, int nb, int& bi, int& bj) 
   bj = r + t;
 }
 
+__host__ __device__ __forceinline__ int tile_index(int bi, int bj, int nb) {
+  return bi * nb - (bi * (bi - 1)) / 2 + (bj - bi);
+}
+
 // LDS byte offset of the 16-byte chunk holding tokens [8 to, 8 to + 8) of
 // channel ch inside one [256 channel][32 token] fp16 panel. The row
 // permutation and chunk XOR keep both the transposing writes (channels
@@ -61,20 +67,42 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {  // (a.hi,
   return (a >> 16) | (b & 0xffff0000u);
 }
 
+// Checked path: for every split either the edge tiles (bi, nb - 1) when d is
+// not a multiple of 256 (all_tiles = 0) or every tile (all_tiles = 1, used
+// when rows are not 16-byte aligned), plus the token tail (n_tokens % 32) of
+// every tile into the extra slot `nsplit`.
+// Tiles are read with bounds-checked 16-byte loads, transposed in registers
+// and stored in a swizzled [channel][token] LDS layout.
 __global__ void __launch_bounds__(SY_THREADS, 1)
-syrk_f16_mfma(const __half* __restrict__ X, int64_t n_tokens, int d, int64_t ldx, int nb, int ntiles,
-              int64_t tokens_per_split, float* __restrict__ partial) {
+syrk_f16_generic(const __half* __restrict__ X, int64_t n_tokens, int64_t n_full, int d, int64_t ldx, int nb,
+                 int ntiles, int64_t tokens_per_split, int nsplit, int n_edge, int all_tiles,
+                 float* __restrict__ partial) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2][SY_T * SY_BK * 2];
 
-  const int tile = blockIdx.x % ntiles;
-  const int split = blockIdx.x / ntiles;
-  int bi, bj;
-  tile_coords(tile, nb, bi, bj);
+  int tile, slot, bi, bj;
+  int64_t kbeg, kend;
+  if (int(blockIdx.x) < n_edge * nsplit) {
+    const int e = blockIdx.x % n_edge;
+    slot = blockIdx.x / n_edge;
+    if (all_tiles) {
+      tile = e;
+      tile_coords(tile, nb, bi, bj);
+    } else {
+      bi = e;
+      bj = nb - 1;
+      tile = tile_index(bi, bj, nb);
+    }
+    kbeg = int64_t(slot) * tokens_per_split;
+    kend = kbeg + tokens_per_split < n_full ? kbeg + tokens_per_split : n_full;
+  } else {
+    tile = blockIdx.x - n_edge * nsplit;
+    tile_coords(tile, nb, bi, bj);
+    slot = nsplit;
+    kbeg = n_full;
+    kend = n_tokens;
+  }
   const bool diag = (bi == bj);
   const int I0 = bi * SY_T, J0 = bj * SY_T;
-  const int64_t kbeg = int64_t(split) * tokens_per_split;
-  int64_t kend = kbeg + tokens_per_split;
-  if (kend > n_tokens) kend = n_tokens;
   const int nsteps = kend > kbeg ? int((kend - kbeg + SY_BK - 1) / SY_BK) : 0;
 
   const int tid = threadIdx.x;
@@ -181,7 +209,7 @@ syrk_f16_mfma(const __half* __restrict__ X, int64_t n_tokens, int d, int64_t ldx
 
   // Partial tile, row-major [256][256]. 32x32 MFMA result layout: lane l holds
   // column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for register r.
-  float* out = partial + (int64_t(split) * ntiles + tile) * (SY_T * SY_T);
+  float* out = partial + (int64_t(slot) * ntiles + tile) * (SY_T * SY_T);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -191,6 +219,157 @@ syrk_f16_mfma(const __half* __restrict__ X, int64_t n_tokens, int d, int64_t ldx
         const int row = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int col = wn * 128 + j * 32 + (lane & 31);
         out[row * SY_T + col] = acc[i][j][r];
+      }
+}
+
+// LDS layout of one panel stage: 32 tokens x 256 fp16 channels, token-major
+// (each token row is its 512 contiguous bytes). Token t sits in slot
+// (t % 16) at half (t / 16): byte (t % 16) * PITCH + (t / 16) * 512. The
+// 64-byte pad per slot pair puts 4 consecutive tokens on 4 distinct 64-byte
+// bank groups, so transposing reads of a 4-token x 16-channel block are
+// conflict free, and one 1 KB direct-to-LDS load instruction (64 lanes x
+// 16 bytes) fills exactly one slot pair (tokens t and t + 16).
+constexpr int S_PITCH = 1088;
+constexpr int S_PANEL = 16 * S_PITCH;  // 17408 bytes
+constexpr int S_STAGE = 2 * S_PANEL;
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+
+__device__ __forceinline__ half8 tr_frag(const unsigned char* lds, int off) {
+  // Two transposing reads: lanes 4r..4r+3 of each 16-lane group fetch token
+  // r of a 4-token x 16-channel block; lane i receives channel i's 4 tokens.
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(lds + off));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(lds + off + 4 * S_PITCH));
+  const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(half8, v);
+}
+
+// Interior tiles (both panels inside the matrix), whole 128-token blocks of
+// 4 steps. Four LDS stages: step s + 3 is loaded while step s is computed.
+constexpr int S_NSTAGE = 4;
+
+__global__ void __launch_bounds__(SY_THREADS, 1)
+syrk_f16_lds(const __half* __restrict__ X, int64_t n_main, int64_t ldx, int nb, int nbf, int n_int,
+             int64_t tokens_per_split, float* __restrict__ partial) {
+  // Separate objects per stage, so the compiler can see that the loads into
+  // one stage never alias the reads of another.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[S_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[S_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[S_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char lds3[S_STAGE];
+
+  const int it = blockIdx.x % n_int;
+  const int split = blockIdx.x / n_int;
+  int bi, bj;
+  tile_coords(it, nbf, bi, bj);
+  const int tile = tile_index(bi, bj, nb);
+  const int ntiles = nb * (nb + 1) / 2;
+  const int I0 = bi * SY_T, J0 = bj * SY_T;
+  const int64_t kbeg = int64_t(split) * tokens_per_split;
+  const int64_t kend = kbeg + tokens_per_split < n_main ? kbeg + tokens_per_split : n_main;
+  const int nsteps = int((kend - kbeg) / SY_BK);  // a multiple of S_NSTAGE
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // Each wave issues 8 direct loads per stage: slot pairs wave + 4u of panel
+  // A (u < 4) and of panel B (u >= 4). A load fills one slot pair: lanes
+  // 0-31 token (pair), lanes 32-63 token (pair + 16), 8 channels per lane.
+  // Per-lane 32-bit element offsets from a per-step uniform base.
+  uint32_t voff[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pair = wave + 4 * (u & 3);
+    const int P0 = u < 4 ? I0 : J0;
+    voff[u] = uint32_t((pair + 16 * (lane >> 5)) * ldx + P0 + 8 * (lane & 31));
+  }
+  auto issue = [&](int step, unsigned char* buf) {
+    const __half* xs = X + (kbeg + int64_t(step) * SY_BK) * ldx;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pair = wave + 4 * (u & 3);
+      unsigned char* l = buf + (u >> 2) * S_PANEL + pair * S_PITCH;
+      __builtin_amdgcn_global_load_lds(xs + voff[u], (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+    }
+  };
+
+  // Per-lane base of the transposing fragment reads: 16-lane group g covers
+  // 16 channels (16 * (g & 1) ..) for tokens 8 * (g >> 1) + [0, 4); within
+  // the group lane 4r + q reads token r, channels 4q .. 4q + 3.
+  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int lane_off = (8 * (g >> 1) + r) * S_PITCH + 2 * (16 * (g & 1) + 4 * q);
+  const int a_base = lane_off + 2 * (wm * 128);
+  const int b_base = S_PANEL + lane_off + 2 * (wn * 128);
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
+
+  auto compute = [&](const unsigned char* base) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      half8 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = tr_frag(base, a_base + 64 * i + 512 * kk);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = tr_frag(base, b_base + 64 * j + 512 * kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  // Wait until this wave's loads of step s have landed: the loads of the
+  // (up to 2) later stages already issued may stay in flight.
+  auto wait_stage = [&](int s) {
+    if (s + 2 < nsteps)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (s + 1 < nsteps)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  if (nsteps > 0) {
+    issue(0, lds0);
+    issue(1, lds1);
+    issue(2, lds2);
+  }
+  for (int s = 0; s < nsteps; s += S_NSTAGE) {
+    wait_stage(s);
+    issue(s + 3, lds3);
+    compute(lds0);
+    wait_stage(s + 1);
+    if (s + 4 < nsteps) issue(s + 4, lds0);
+    compute(lds1);
+    wait_stage(s + 2);
+    if (s + 5 < nsteps) issue(s + 5, lds1);
+    compute(lds2);
+    wait_stage(s + 3);
+    if (s + 6 < nsteps) issue(s + 6, lds2);
+    compute(lds3);
+  }
+
+  // Partial tile, row-major [256][256]. 32x32 MFMA result layout: lane l holds
+  // column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for register r.
+  float* out = partial + (int64_t(split) * ntiles + tile) * (SY_T * SY_T);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = wm * 128 + i * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+        const int col = wn * 128 + j * 32 + (lane & 31);
+        out[row * SY_T + col] = acc[i][j][rr];
       }
 }
 
@@ -259,8 +438,18 @@ syrk_reduce(const float* __restrict__ partial, int T, int nb, int ntiles, int ns
     const int gr = R0 + r, gc = C0 + c;
     double s = 0.0;
     if (gr < d && gc < d) {
+      // Fixed order: splits 0, 1, 2, ... (loads batched 8 at a time).
       const int64_t off = int64_t(tile) * T * T + int64_t(gr - bi * T) * T + (gc - bj * T);
-      for (int sp = 0; sp < nsplit; ++sp) s += double(partial[int64_t(sp) * ntiles * T * T + off]);
+      const int64_t stride = int64_t(ntiles) * T * T;
+      int sp = 0;
+      for (; sp + 8 <= nsplit; sp += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = partial[(sp + u) * stride + off];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += double(v[u]);
+      }
+      for (; sp < nsplit; ++sp) s += double(partial[sp * stride + off]);
     }
     blk[r][c] = s;
   }
@@ -289,27 +478,39 @@ __global__ void fill_zero_f32(float* p, int64_t n) {
 }
 
 struct SyrkPlan {
-  int T, nb, ntiles, nsplit;
-  int64_t tokens_per_split;
+  int T, nb, ntiles, nsplit, nslot;
+  int nbf, n_int, n_edge;  // fp16: interior blocks/tiles, edge tiles
+  int64_t tokens_per_split, n_full;
   size_t ws_bytes;
 };
 
+// Token splits over the whole 32-token steps ([0, n_full)): enough
+// workgroups to keep 256 CUs busy for several rounds and at least 4 partial
+// sums per tile. fp16 inputs put the token tail (n_tokens % 32) of every
+// tile in one extra slot; fp32 inputs split all tokens.
 SyrkPlan plan_syrk(int64_t n_tokens, int64_t d, int xdtype) {
   SyrkPlan p{};
-  const int bk = xdtype == GPTQ_F16 ? SY_BK : SYF_BK;
-  p.T = xdtype == GPTQ_F16 ? SY_T : SYF_T;
+  const bool f16 = xdtype == GPTQ_F16;
+  const int bk = f16 ? SY_BK : SYF_BK;
+  p.T = f16 ? SY_T : SYF_T;
   p.nb = int((d + p.T - 1) / p.T);
   p.ntiles = p.nb * (p.nb + 1) / 2;
-  const int64_t ksteps = (n_tokens + bk - 1) / bk;
-  // Enough workgroups to keep 256 CUs busy for several rounds, at least 4
-  // partial sums for accuracy, never more splits than token steps.
+  // fp16: splits cover whole blocks of 4 steps (128 tokens), the rest of the
+  // tokens is the tail.
+  const int unit = f16 ? bk * S_NSTAGE : bk;
+  p.n_full = f16 ? (n_tokens / unit) * unit : n_tokens;
+  const int64_t ksteps = (p.n_full + unit - 1) / unit;
   int64_t want = (2048 + p.ntiles - 1) / p.ntiles;
   if (want < 4) want = 4;
   if (want > ksteps) want = ksteps;
   if (want < 1) want = 1;
-  p.tokens_per_split = ((ksteps + want - 1) / want) * bk;
-  p.nsplit = n_tokens > 0 ? int((n_tokens + p.tokens_per_split - 1) / p.tokens_per_split) : 0;
-  p.ws_bytes = align_up(size_t(p.nsplit) * p.ntiles * p.T * p.T * sizeof(float), 256);
+  p.tokens_per_split = ((ksteps + want - 1) / want) * unit;
+  p.nsplit = p.n_full > 0 ? int((p.n_full + p.tokens_per_split - 1) / p.tokens_per_split) : 0;
+  p.nslot = p.nsplit + ((f16 && n_tokens > p.n_full) ? 1 : 0);
+  p.nbf = f16 ? int(d / p.T) : 0;
+  p.n_int = p.nbf * (p.nbf + 1) / 2;
+  p.n_edge = (f16 && d % p.T != 0) ? p.nb : 0;
+  p.ws_bytes = align_up(size_t(p.nslot) * p.ntiles * p.T * p.T * sizeof(float), 256);
   return p;
 }
 
@@ -339,17 +540,40 @@ extern "C" int gptq_hessian_accumulate(const void* X, int xdtype, int64_t n_toke
   const SyrkPlan p = plan_syrk(n_tokens, d, xdtype);
   if (ws == nullptr || ws_bytes < p.ws_bytes) return GPTQ_E_WORKSPACE;
   float* partial = static_cast<float*>(ws);
-  const dim3 grid(unsigned(int64_t(p.ntiles) * p.nsplit));
   if (xdtype == GPTQ_F16) {
-    hipLaunchKernelGGL(syrk_f16_mfma, grid, dim3(SY_THREADS), 0, s, static_cast<const __half*>(X), n_tokens,
-                       int(d), ldx, p.nb, p.ntiles, p.tokens_per_split, partial);
+    const __half* Xh = static_cast<const __half*>(X);
+    // Direct-to-LDS loads need 16-byte aligned rows.
+    // (and per-lane offsets below 32 tokens x ldx must fit in 32 bits).
+    const bool direct = ((ldx & 7) == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0) && ldx < (int64_t(1) << 26);
+    int n_edge = p.n_edge, nbf = p.nbf, n_int = p.n_int;
+    if (!direct) {  // every tile takes the checked path
+      n_edge = 0;
+      nbf = 0;
+      n_int = 0;
+    }
+    if (n_int > 0 && p.nsplit > 0) {
+      hipLaunchKernelGGL(syrk_f16_lds, dim3(unsigned(int64_t(n_int) * p.nsplit)), dim3(SY_THREADS), 0, s, Xh,
+                         p.n_full, ldx, p.nb, nbf, n_int, p.tokens_per_split, partial);
+      if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+    }
+    // Checked path: edge tiles of every split (all tiles when the direct
+    // path is unusable), plus the token tail of every tile.
+    const int gen_tiles_main = direct ? n_edge : p.ntiles;
+    const int64_t n_gen = int64_t(gen_tiles_main) * p.nsplit + (p.nslot > p.nsplit ? p.ntiles : 0);
+    if (n_gen > 0) {
+      hipLaunchKernelGGL(syrk_f16_generic, dim3(unsigned(n_gen)), dim3(SY_THREADS), 0, s, Xh, n_tokens, p.n_full,
+                         int(d), ldx, p.nb, p.ntiles, p.tokens_per_split, p.nsplit, gen_tiles_main,
+                         direct ? 0 : 1, partial);
+      if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+    }
   } else {
-    hipLaunchKernelGGL(syrk_f32_valu, grid, dim3(256), 0, s, static_cast<const float*>(X), n_tokens, int(d), ldx,
-                       p.nb, p.ntiles, p.tokens_per_split, partial);
+    hipLaunchKernelGGL(syrk_f32_valu, dim3(unsigned(int64_t(p.ntiles) * p.nsplit)), dim3(256), 0, s,
+                       static_cast<const float*>(X), n_tokens, int(d), ldx, p.nb, p.ntiles, p.tokens_per_split,
+                       partial);
+    if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }
-  if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   const int nob = int((d + 31) / 32);
   hipLaunchKernelGGL(syrk_reduce, dim3(unsigned(nob * nob)), dim3(256), 0, s, partial, p.T, p.nb, p.ntiles,
-                     p.nsplit, int(d), H, accumulate);
+                     p.nslot, int(d), H, accumulate);
   return launch_status();
 }

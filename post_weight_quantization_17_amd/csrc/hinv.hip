@@ -90,48 +90,61 @@ hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, d
 // to the trailing block (a_ic -= m_i a_cj, c in (j, i]) and to the unit-lower
 // inverse Y (y_ic -= m_i y_jc, c <= j). Then L_ij = a_ij / sqrt(a_jj) and
 // L^-1_ic = y_ic / sqrt(a_ii).
+// Thread t owns row i = t / 4 and columns c = t % 4 + 4 m (m < 16); each step
+// issues all of its LDS loads before any store, so a step costs one LDS
+// round trip plus one barrier.
 __global__ void __launch_bounds__(256)
 hinv_diag(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, double* __restrict__ Lbuf,
           int32_t* __restrict__ info) {
-  __shared__ double a[NB][NB + 1];
-  __shared__ double y[NB][NB + 1];
+  constexpr int P = NB + 1;
+  constexpr int YOFF = NB * P;       // y follows a in one array
+  constexpr int DUMP = 2 * NB * P;   // per-thread slots for masked-off stores
+  __shared__ double ay[2 * NB * P + 256];
   __shared__ double sq[NB];
   const int tid = threadIdx.x;
+#pragma unroll
   for (int e = tid; e < NB * NB; e += 256) {
     const int i = e / NB, c = e % NB;
-    double v = 0.0;
-    if (i < kb && c <= i) v = A[int64_t(k0 + i) * d + k0 + c];
-    a[i][c] = v;
-    y[i][c] = (i == c) ? 1.0 : 0.0;
+    const bool in = i < kb && c <= i;
+    const double v = A[in ? int64_t(k0 + i) * d + k0 + c : int64_t(k0) * d + k0];
+    ay[i * P + c] = in ? v : 0.0;
+    ay[YOFF + i * P + c] = (i == c) ? 1.0 : 0.0;
   }
   __syncthreads();
+  const int i = tid >> 2, c0 = tid & 3;
   for (int j = 0; j < kb; ++j) {
-    const double piv = a[j][j];
+    const double piv = ay[j * P + j];
     if (tid == 0 && !(piv > 0.0)) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + j)));
-    const double inv = 1.0 / piv;
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int i = e / NB, c = e % NB;
-      if (i <= j || i >= kb || c > i) continue;
-      const double m = a[i][j] * inv;
-      if (c > j)
-        a[i][c] -= m * a[c][j];
-      else
-        y[i][c] -= m * y[j][c];
+    const bool row_act = i > j && i < kb;
+    const double m = ay[i * P + j] / piv;
+    int io[NB / 4], ic[NB / 4];
+    double other[NB / 4], cur[NB / 4];
+#pragma unroll
+    for (int t = 0; t < NB / 4; ++t) {
+      const int c = c0 + 4 * t;
+      const bool lower = c > j;
+      io[t] = lower ? c * P + j : YOFF + j * P + c;        // a[c][j] or y[j][c]
+      ic[t] = lower ? i * P + c : YOFF + i * P + c;        // a[i][c] or y[i][c]
+      if (!(row_act && c <= i)) ic[t] = DUMP + tid;        // masked off: private slot
+      other[t] = ay[io[t]];
+      cur[t] = ay[ic[t]];
     }
+#pragma unroll
+    for (int t = 0; t < NB / 4; ++t) ay[ic[t]] = cur[t] - m * other[t];
     __syncthreads();
   }
-  if (tid < kb) sq[tid] = sqrt(a[tid][tid]);
+  if (tid < kb) sq[tid] = sqrt(ay[tid * P + tid]);
   __syncthreads();
   for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, c = e % NB;
+    const int r = e / NB, c = e % NB;
     double l = 0.0, x = 0.0;
-    if (i < kb && c <= i) {
-      l = (c == i) ? sq[i] : a[i][c] / sq[c];
-      x = y[i][c] / sq[i];
-      A[int64_t(k0 + i) * d + k0 + c] = l;
-      R[int64_t(k0 + i) * d + k0 + c] = x;
+    if (r < kb && c <= r) {
+      l = (c == r) ? sq[r] : ay[r * P + c] / sq[c];
+      x = ay[YOFF + r * P + c] / sq[r];
+      A[int64_t(k0 + r) * d + k0 + c] = l;
+      R[int64_t(k0 + r) * d + k0 + c] = x;
     }
-    Lbuf[i * NB + c] = x;  // X_kk, zero outside the kb x kb lower triangle
+    Lbuf[r * NB + c] = x;  // X_kk, zero outside the kb x kb lower triangle
   }
 }
 
@@ -192,9 +205,20 @@ hinv_panel(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb
   if (int(blockIdx.x) < nrow) {
     const int r0 = k1 + NB * blockIdx.x;
     // left: A[r0+i][k0+m]; right[m][j] = X_kk[j][m]
-    for (int e = tid; e < NB * NB; e += 256) {
+    double v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = tid + 256 * t;
       const int i = e / NB, m = e % NB;
-      Ls[i][m] = (r0 + i < d && m < kb) ? A[int64_t(r0 + i) * d + k0 + m] : 0.0;
+      const bool ok = r0 + i < d && m < kb;
+      v[t] = A[ok ? int64_t(r0 + i) * d + k0 + m : 0];
+      v[t] = ok ? v[t] : 0.0;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = tid + 256 * t;
+      const int i = e / NB, m = e % NB;
+      Ls[i][m] = v[t];
       Rs[m][i] = Lbuf[i * NB + m];
     }
     __syncthreads();
@@ -205,10 +229,21 @@ hinv_panel(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb
   } else {
     const int c0 = NB * (blockIdx.x - nrow);
     // left: X_kk[i][m]; right[m][c] = R[k0+m][c0+c]
-    for (int e = tid; e < NB * NB; e += 256) {
+    double v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = tid + 256 * t;
+      const int i = e / NB, c = e % NB;
+      const bool ok = i < kb && c0 + c < k0;
+      v[t] = R[ok ? int64_t(k0 + i) * d + c0 + c : 0];
+      v[t] = ok ? v[t] : 0.0;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int e = tid + 256 * t;
       const int i = e / NB, c = e % NB;
       Ls[i][c] = Lbuf[i * NB + c];
-      Rs[i][c] = (i < kb && c0 + c < k0) ? R[int64_t(k0 + i) * d + c0 + c] : 0.0;
+      Rs[i][c] = v[t];
     }
     __syncthreads();
     tile_mma(Ls, Rs, Kp, acc);
@@ -219,23 +254,104 @@ hinv_panel(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb
 }
 
 // ----------------------------------------------------------- update step
-// Blocks [0, nA): lower tiles (ti >= tj) of the trailing matrix at k1:
+// 128x128 output tiles, K = kb <= 64. Each of the 4 waves owns a 64x64
+// quarter (4x4 MFMA 16x16 blocks). Operands are staged with 16-byte loads,
+// all issued before the first LDS store.
+constexpr int UT = 128;
+constexpr int UP = 66;   // pitch (doubles) of the [128][K] left operand
+constexpr int UQ = 132;  // pitch (doubles) of the [K][128] right operand
+
+// Stages a 128-row x 64-col fp64 block of M (rows r0.., cols k0..) into LDS,
+// Ls[r][k] (transpose = false) or Ls[k][r] (transpose = true). Elements with
+// row >= rmax or col >= k0 + kmax read as zero. Every thread issues its 32
+// loads from clamped in-bounds addresses before storing anything.
+template <bool TRANSPOSE, typename Dst>
+__device__ __forceinline__ void stage_block(Dst Ls, const double* __restrict__ M, int d, int r0, int rmax, int k0,
+                                            int kmax) {
+  const int tid = threadIdx.x;
+  double v[32];
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int e = tid + 256 * t;  // 8192 elements = 128 rows x 64 cols
+    const int r = e >> 6, k = e & 63;
+    const bool ok = (r0 + r < rmax) && (k < kmax);
+    v[t] = M[ok ? int64_t(r0 + r) * d + k0 + k : 0];
+    v[t] = ok ? v[t] : 0.0;
+  }
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int e = tid + 256 * t;
+    const int r = e >> 6, k = e & 63;
+    if (TRANSPOSE)
+      Ls[k][r] = v[t];
+    else
+      Ls[r][k] = v[t];
+  }
+}
+
+__device__ __forceinline__ void tile128_mma(const double (*Ls)[UP], const double (*Rs)[UQ], int K, doublex4 acc[4][4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  for (int k = 0; k < K; k += 4) {
+    double av[4], bv[4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) av[ii] = Ls[wr * 64 + ii * 16 + (lane & 15)][k + (lane >> 4)];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) bv[jj] = Rs[k + (lane >> 4)][wc * 64 + jj * 16 + (lane & 15)];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        acc[ii][jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii], bv[jj], acc[ii][jj], 0, 0, 0);
+  }
+}
+
+// M[tile element] -= acc for the elements `keep` selects. All 64 loads are
+// issued unconditionally (masked-off ones read M[0]) before any store, so
+// the tile costs one memory round trip; only the stores are masked.
+template <typename Keep>
+__device__ __forceinline__ void rmw_sub(double* __restrict__ M, int d, int r0, int c0, doublex4 acc[4][4], Keep keep) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  double old[4][4][4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gi = r0 + wr * 64 + ii * 16 + (lane >> 4) + 4 * r;
+        const int gj = c0 + wc * 64 + jj * 16 + (lane & 15);
+        old[ii][jj][r] = M[keep(gi, gj) ? int64_t(gi) * d + gj : 0];
+      }
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gi = r0 + wr * 64 + ii * 16 + (lane >> 4) + 4 * r;
+        const int gj = c0 + wc * 64 + jj * 16 + (lane & 15);
+        if (keep(gi, gj)) M[int64_t(gi) * d + gj] = old[ii][jj][r] - acc[ii][jj][r];
+      }
+}
+
+// Blocks [0, nA): lower 128-tiles (ti >= tj) of the trailing matrix at k1:
 //   A_ij -= L_i L_j^T.
-// Blocks [nA, nA + nT * nC): R[k1 + 64 ti, 64 tc] -= L_i X[k, 64 tc].
+// Blocks [nA, nA + nT * nC): R[k1 + 128 ti, 128 tc] -= L_i X[k, 128 tc].
 __global__ void __launch_bounds__(256)
 hinv_update(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, int nT, int nC) {
-  __shared__ double Ls[NB][LP];
-  __shared__ double Rs[NB][LP];
-  const int tid = threadIdx.x;
+  __shared__ double Ls[UT][UP];
+  __shared__ double Rs[NB][UQ];
   const int k1 = k0 + kb;
   const int Kp = (kb + 3) & ~3;
   const int nA = nT * (nT + 1) / 2;
   int b = blockIdx.x;
-  doublex4 acc[2][2];
+  doublex4 acc[4][4];
 #pragma unroll
-  for (int ii = 0; ii < 2; ++ii)
+  for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
+    for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
   if (b < nA) {
     int ti = 0;
     while (b > ti) {
@@ -243,36 +359,40 @@ hinv_update(double* __restrict__ A, double* __restrict__ R, int d, int k0, int k
       ++ti;
     }
     const int tj = b;
-    const int r0 = k1 + NB * ti, c0 = k1 + NB * tj;
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int i = e / NB, m = e % NB;
-      Ls[i][m] = (r0 + i < d && m < kb) ? A[int64_t(r0 + i) * d + k0 + m] : 0.0;
-      Rs[m][i] = (c0 + i < d && m < kb) ? A[int64_t(c0 + i) * d + k0 + m] : 0.0;
-    }
+    const int r0 = k1 + UT * ti, c0 = k1 + UT * tj;
+    stage_block<false>(Ls, A, d, r0, d, k0, kb);
+    stage_block<true>(Rs, A, d, c0, d, k0, kb);  // Rs[m][j] = L[c0 + j][k0 + m]
     __syncthreads();
-    tile_mma(Ls, Rs, Kp, acc);
-    tile_for_each(acc, [&](int i, int j, double v) {
-      if (r0 + i < d && c0 + j < d && c0 + j <= r0 + i) A[int64_t(r0 + i) * d + c0 + j] -= v;
-    });
+    tile128_mma(Ls, Rs, Kp, acc);
+    rmw_sub(A, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj <= gi; });
   } else {
     b -= nA;
     const int ti = b / nC, tc = b % nC;
-    const int r0 = k1 + NB * ti, c0 = NB * tc;
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int i = e / NB, m = e % NB;
-      Ls[i][m] = (r0 + i < d && m < kb) ? A[int64_t(r0 + i) * d + k0 + m] : 0.0;
-    }
-    for (int e = tid; e < NB * NB; e += 256) {
-      const int m = e / NB, c = e % NB;
-      // X[k, :k1] is block row k of X: lower triangular inside the diagonal
-      // block (R's upper part is never written, so it is masked here).
-      Rs[m][c] = (m < kb && c0 + c < k1 && c0 + c <= k0 + m) ? R[int64_t(k0 + m) * d + c0 + c] : 0.0;
+    const int r0 = k1 + UT * ti, c0 = UT * tc;
+    stage_block<false>(Ls, A, d, r0, d, k0, kb);
+    {
+      // Rs[m][c] = X[k0 + m][c0 + c]; X is lower triangular inside the
+      // diagonal block (R's upper part is never written, so it is masked).
+      const int tid = threadIdx.x;
+      double v[32];
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const int e = tid + 256 * t;  // 64 rows x 128 cols
+        const int m = e >> 7, c = e & 127;
+        const int g = c0 + c;
+        const bool ok = m < kb && g < k1 && g <= k0 + m;
+        v[t] = R[ok ? int64_t(k0 + m) * d + g : 0];
+        v[t] = ok ? v[t] : 0.0;
+      }
+#pragma unroll
+      for (int t = 0; t < 32; ++t) {
+        const int e = tid + 256 * t;
+        Rs[e >> 7][e & 127] = v[t];
+      }
     }
     __syncthreads();
-    tile_mma(Ls, Rs, Kp, acc);
-    tile_for_each(acc, [&](int i, int c, double v) {
-      if (r0 + i < d && c0 + c < k1) R[int64_t(r0 + i) * d + c0 + c] -= v;
-    });
+    tile128_mma(Ls, Rs, Kp, acc);
+    rmw_sub(R, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj < k1; });
   }
 }
 
@@ -334,8 +454,8 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     if (nrow + ncol > 0)
       hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, di, k0, kb, w.Lbuf,
                          nrow);
-    const int nT = nrow;
-    const int nC = (k1 + NB - 1) / NB;
+    const int nT = (di - k1 + UT - 1) / UT;
+    const int nC = (k1 + UT - 1) / UT;
     const int nblk = nT * (nT + 1) / 2 + nT * nC;
     if (nblk > 0)
       hipLaunchKernelGGL(hinv_update, dim3(unsigned(nblk)), dim3(256), 0, s, w.A, w.R, di, k0, kb, nT, nC);

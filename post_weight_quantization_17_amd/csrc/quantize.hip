@@ -130,34 +130,65 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
     const bool first = (i1 == 0);
 
     // 1. U block (upper part; padded columns act as identity rows) and W block.
-    for (int e = tid; e < QB * QB; e += QT) {
-      const int k = e >> 7, j = e & (QB - 1);
-      float v;
-      if (k < nvalid && j < nvalid)
-        v = j >= k ? U[size_t(i1 + k) * d_col + i1 + j] : 0.f;
-      else
-        v = (k == j) ? 1.f : 0.f;
-      Ud[k][j] = v;
+    if (vec4 && nvalid == QB) {
+      // Full aligned block: 2 x 8 float4 loads per thread, each batch in
+      // flight before its LDS stores; the strict lower triangle is zeroed.
+      const int k0 = tid >> 5, j0 = (tid & 31) * 4;
+      const float* src = U + size_t(i1 + k0) * d_col + i1 + j0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        floatx4 uv[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) uv[t] = load4(src + size_t(8 * (t + 8 * half)) * d_col);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int k = k0 + 8 * (t + 8 * half);
+          floatx4 v = uv[t];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = (j0 + u >= k) ? v[u] : 0.f;
+          *reinterpret_cast<float4*>(&Ud[k][j0]) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    } else {
+      for (int e = tid; e < QB * QB; e += QT) {
+        const int k = e >> 7, j = e & (QB - 1);
+        float v;
+        if (k < nvalid && j < nvalid)
+          v = j >= k ? U[size_t(i1 + k) * d_col + i1 + j] : 0.f;
+        else
+          v = (k == j) ? 1.f : 0.f;
+        Ud[k][j] = v;
+      }
     }
-    float wr[QM], cr[QM], er[QM];
+    float wr[QM];
 #pragma unroll
     for (int m = 0; m < QM; ++m) {
       const int jl = 16 * m + sub;
       float v = 0.f;
       if (row_ok && jl < nvalid) v = first ? to_f(W[rbase + i1 + jl]) : Wf[rbase + i1 + jl];
       wr[m] = v;
-      cr[m] = 0.f;
-      er[m] = 0.f;
     }
     __syncthreads();
     if (tid < QB) dinv[tid] = 1.f / Ud[tid][tid];
     __syncthreads();
 
-    // 2. The 128 sequential column steps.
+    // 2. The 128 sequential column steps. Row q+1 of the U block and
+    //    1/U_{q+1,q+1} are loaded while step q runs; the empty asm with a
+    //    memory clobber keeps the steps in program order (no store merging
+    //    or load hoisting across steps, which would lengthen live ranges).
+    float uc[QM], un[QM];
+    float dc = dinv[0], dn = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < QM; ++mm) uc[mm] = Ud[0][16 * mm + sub];
     static_for<0, QB>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       constexpr int m = q / 16;
       constexpr int o = q % 16;
+      if constexpr (q + 1 < QB) {
+#pragma unroll
+        for (int mm = (q + 1) / 16; mm < QM; ++mm) un[mm] = Ud[q + 1][16 * mm + sub];
+        dn = dinv[q + 1];
+      }
       if constexpr (o == 0) {
         if (group > 0 && q < nvalid && (i1 + q) % group == 0) {
           float mn = 0.f, mx = 0.f;
@@ -191,27 +222,29 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       c = fminf(fmaxf(c, 0.f), maxq);
       const float what = s * (c - z);
       const float err = x - what;
-      const float e = err * dinv[q];
-      lacc = fma(0.5 * double(e), double(e), lacc);
-      // Keep the owner's code and error as they are produced (otherwise the
-      // compiler defers the selects and keeps all 16 steps' values live).
-      cr[m] = sub == o ? c : cr[m];
-      er[m] = sub == o ? e : er[m];
-      asm volatile("" : "+v"(cr[m]), "+v"(er[m]), "+v"(lacc));
+      const float e = err * dc;
 #pragma unroll
-      for (int mm = m; mm < QM; ++mm) wr[mm] = fmaf(-e, Ud[q][16 * mm + sub], wr[mm]);
+      for (int mm = m; mm < QM; ++mm) wr[mm] = fmaf(-e, uc[mm], wr[mm]);
+      lacc = fma(0.5 * double(e), double(e), lacc);
+      // Every lane of the row holds the same code and error: all 16 store
+      // the same value to the row's LDS slot, so no owner test is needed.
+      Cs[rloc][q] = uint8_t(c);
+      Es[rloc][q] = e;
+      if constexpr (q + 1 < QB) {
+#pragma unroll
+        for (int mm = (q + 1) / 16; mm < QM; ++mm) uc[mm] = un[mm];
+        dc = dn;
+      }
+      asm volatile("" ::: "memory");
     });
 
-    // 3. Codes, packed words, errors.
+    // 3. Codes, packed words (the errors are already in Es).
+    __syncthreads();
 #pragma unroll
     for (int m = 0; m < QM; ++m) {
       const int jl = 16 * m + sub;
-      const uint8_t cv = uint8_t(cr[m]);
-      if (row_ok && jl < nvalid) codes[rbase + i1 + jl] = cv;
-      Cs[rloc][jl] = cv;
-      Es[rloc][jl] = er[m];
+      if (row_ok && jl < nvalid) codes[rbase + i1 + jl] = Cs[rloc][jl];
     }
-    __syncthreads();
     {
       const int nwb = (nvalid * bits + 31) / 32;
       const int wbase = (i1 * bits) / 32;
@@ -245,18 +278,31 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
 #pragma unroll
           for (int t = 0; t < 4; ++t) acc[t][r] = v[t];
         }
-#pragma unroll 8
-        for (int t = 0; t < QB / 4; ++t) {
-          const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
-          const size_t uoff = size_t(i1 + 4 * t + lk) * d_col + col;
+        // B operands U[i1 + 4t + lk][col .. col + 3] through a 16-deep
+        // register ring: the load for step t + 16 is issued as step t retires.
+        const float* ub = U + size_t(i1 + lk) * d_col + col;
+        const uint32_t ustep = uint32_t(4 * d_col);
+        auto ldb = [&](int t) -> floatx4 {
+          const float* p = ub + uint32_t(t) * ustep;
           floatx4 b = {0.f, 0.f, 0.f, 0.f};
           if (full) {
-            b = load4(U + uoff);
+            b = load4(p);
           } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-              if (col + u < d_col) b[u] = U[uoff + u];
+              if (col + u < d_col) b[u] = p[u];
           }
+          return b;
+        };
+        constexpr int RING = 8;
+        floatx4 ring[RING];
+#pragma unroll
+        for (int t = 0; t < RING; ++t) ring[t] = ldb(t);
+#pragma unroll
+        for (int t = 0; t < QB / 4; ++t) {
+          const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
+          const floatx4 b = ring[t % RING];
+          if (t + RING < QB / 4) ring[t % RING] = ldb(t + RING);
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[v], 0, 0, 0);
         }
