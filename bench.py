@@ -51,6 +51,30 @@ def upload_activations(cfg, torch, dev):
     return X
 
 
+def hessian_traffic_bytes():
+    """HBM bytes per Hessian-stage call from the committed counter summary.
+
+    profiles/hessian_syrk_attn4096_counters.md holds FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch, summed over the stage's two kernels), the
+    copy-calibration scales and the SHA-256 of the kernel source they were
+    taken with. Returns None when that source has changed since.
+    """
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", "hessian_syrk_attn4096_counters.md")
+    src = os.path.join(ROOT, "post_weight_quantization_17_amd", "csrc", "hessian.hip")
+    try:
+        text = open(path).read()
+        m = re.search(r"bench-traffic: source_sha256=(\w+) fetch_kib=(\S+) write_kib=(\S+) fetch_scale=(\S+) write_scale=(\S+)", text)
+        if not m or hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(1):
+            return None
+        fk, wk, fs, ws = (float(m.group(i)) for i in range(2, 6))
+        return (fk * fs + wk * ws) * 1024.0
+    except OSError:
+        return None
+
+
 def cpu_baseline(cfg, budget_rows=128, budget_tokens=16384):
     """The float64 oracle timed on a bounded sample of the same layer.
 
@@ -203,14 +227,16 @@ def main():
     syrk_tflops = syrk_flops / (t_h * 1e-3) / 1e12
     trail_flops = float(sum(2.0 * cfg.d_row * cfg.block * (d - i2) for i2 in range(cfg.block, d, cfg.block)))
     chol_flops = 2.0 * d**3 / 3.0
+    traffic = hessian_traffic_bytes() if cfg.name == "attn_proj_4096x4096_4bit_g128" else None
     roofline = {
         "bound": "mfma",
-        "kernel": "Hessian SYRK stage (syrk_f16_mfma + fixed-order split reduction)",
+        "kernel": "Hessian stage: syrk_f16_lds + syrk_reduce (one gptq_hessian_accumulate call)",
         "achieved": syrk_tflops,
         "peak": PEAK_FP16_MFMA / 1e12,
         "unit": "TFLOP/s",
         "frac": syrk_tflops * 1e12 / PEAK_FP16_MFMA,
-        "traffic": None,
+        "traffic": traffic,
+        "traffic_unit": "bytes",
         "per_launch_flops": syrk_flops,
     }
     out = {

@@ -24,6 +24,8 @@
 // R starts as the identity; block row i of R becomes block row i of X once
 // its own panel step runs. Each step's products are 64x64 tiles on the fp64
 // MFMA (v_mfma_f64_16x16x4f64).
+#include <utility>
+
 #include "gptq_common.h"
 
 namespace gptq {
@@ -89,62 +91,89 @@ hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, d
 // step j eliminates column j with multipliers m_i = a_ij / a_jj, applied both
 // to the trailing block (a_ic -= m_i a_cj, c in (j, i]) and to the unit-lower
 // inverse Y (y_ic -= m_i y_jc, c <= j). Then L_ij = a_ij / sqrt(a_jj) and
-// L^-1_ic = y_ic / sqrt(a_ii).
-// Thread t owns row i = t / 4 and columns c = t % 4 + 4 m (m < 16); each step
-// issues all of its LDS loads before any store, so a step costs one LDS
-// round trip plus one barrier.
+// L^-1_ic = y_ic / sqrt(a_ii). Rows and columns past kb act as identity.
+//
+// Thread t owns row i = t / 4, columns c = t % 4 + 4 m (m < 16) of both a and
+// y, in registers, for all 64 (fully unrolled) steps. Step j only exchanges
+// column j of a and row j of y through LDS (double buffered: one barrier).
+template <int Q, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (Q < N) {
+    f(std::integral_constant<int, Q>{});
+    static_for<Q + 1, N>(f);
+  }
+}
+
 __global__ void __launch_bounds__(256)
 hinv_diag(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, double* __restrict__ Lbuf,
           int32_t* __restrict__ info) {
-  constexpr int P = NB + 1;
-  constexpr int YOFF = NB * P;       // y follows a in one array
-  constexpr int DUMP = 2 * NB * P;   // per-thread slots for masked-off stores
-  __shared__ double ay[2 * NB * P + 256];
-  __shared__ double sq[NB];
+  __shared__ double acol[2][NB];
+  __shared__ double yrow[2][NB];
+  __shared__ double dg[NB];
   const int tid = threadIdx.x;
+  const int i_ = tid >> 2, c0_ = tid & 3;
+  double av[NB / 4], yv[NB / 4];
+  const int i = i_, c0 = c0_;
 #pragma unroll
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int i = e / NB, c = e % NB;
+  for (int t = 0; t < NB / 4; ++t) {
+    const int c = c0 + 4 * t;
     const bool in = i < kb && c <= i;
     const double v = A[in ? int64_t(k0 + i) * d + k0 + c : int64_t(k0) * d + k0];
-    ay[i * P + c] = in ? v : 0.0;
-    ay[YOFF + i * P + c] = (i == c) ? 1.0 : 0.0;
+    av[t] = in ? v : (i == c ? 1.0 : 0.0);
+    yv[t] = (i == c) ? 1.0 : 0.0;
   }
-  __syncthreads();
-  const int i = tid >> 2, c0 = tid & 3;
-  for (int j = 0; j < kb; ++j) {
-    const double piv = ay[j * P + j];
-    if (tid == 0 && !(piv > 0.0)) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + j)));
-    const bool row_act = i > j && i < kb;
-    const double m = ay[i * P + j] / piv;
-    int io[NB / 4], ic[NB / 4];
-    double other[NB / 4], cur[NB / 4];
+  static_for<0, NB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    constexpr int b = j & 1;
+    // Fresh copies of the lane indices each step, so the compiler computes
+    // this step's comparisons here instead of keeping all 64 steps' live.
+    int i = i_, c0 = c0_;
+    asm volatile("" : "+v"(i), "+v"(c0));
+    if (c0 == (j & 3)) acol[b][i] = av[j >> 2];  // column j of a (all rows)
+    if (i == j) {
 #pragma unroll
-    for (int t = 0; t < NB / 4; ++t) {
-      const int c = c0 + 4 * t;
-      const bool lower = c > j;
-      io[t] = lower ? c * P + j : YOFF + j * P + c;        // a[c][j] or y[j][c]
-      ic[t] = lower ? i * P + c : YOFF + i * P + c;        // a[i][c] or y[i][c]
-      if (!(row_act && c <= i)) ic[t] = DUMP + tid;        // masked off: private slot
-      other[t] = ay[io[t]];
-      cur[t] = ay[ic[t]];
+      for (int t = 0; t < NB / 4; ++t) yrow[b][c0 + 4 * t] = yv[t];  // row j of y
     }
-#pragma unroll
-    for (int t = 0; t < NB / 4; ++t) ay[ic[t]] = cur[t] - m * other[t];
     __syncthreads();
-  }
-  if (tid < kb) sq[tid] = sqrt(ay[tid * P + tid]);
-  __syncthreads();
-  for (int e = tid; e < NB * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    double l = 0.0, x = 0.0;
-    if (r < kb && c <= r) {
-      l = (c == r) ? sq[r] : ay[r * P + c] / sq[c];
-      x = ay[YOFF + r * P + c] / sq[r];
-      A[int64_t(k0 + r) * d + k0 + c] = l;
-      R[int64_t(k0 + r) * d + k0 + c] = x;
+    const double piv = acol[b][j];
+    if (tid == 0) {
+      dg[j] = piv;
+      if (j < kb && !(piv > 0.0)) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + j)));
     }
-    Lbuf[r * NB + c] = x;  // X_kk, zero outside the kb x kb lower triangle
+    const double m = i > j ? acol[b][i] / piv : 0.0;
+    static_for<0, NB / 4>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      const int c = c0 + 4 * t;
+      if constexpr (4 * t > j) {
+        av[t] = fma(-m, acol[b][c], av[t]);
+      } else if constexpr (4 * t + 3 <= j) {
+        yv[t] = fma(-m, yrow[b][c], yv[t]);
+      } else {
+        const bool up = c > j;
+        const double o = up ? acol[b][c] : yrow[b][c];
+        const double nv = fma(-m, o, up ? av[t] : yv[t]);
+        av[t] = up ? nv : av[t];
+        yv[t] = up ? yv[t] : nv;
+      }
+    });
+    // Materialize this step's updates now (otherwise the compiler defers the
+    // fma chains and keeps every step's operands live).
+#pragma unroll
+    for (int t = 0; t < NB / 4; ++t) asm volatile("" : "+v"(av[t]), "+v"(yv[t]));
+  });
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NB / 4; ++t) {
+    const int c = c0 + 4 * t;
+    double x = 0.0;
+    if (i < kb && c <= i) {
+      const double sc = sqrt(dg[c]), si = sqrt(dg[i]);
+      const double l = (c == i) ? si : av[t] / sc;
+      x = yv[t] / si;
+      A[int64_t(k0 + i) * d + k0 + c] = l;
+      R[int64_t(k0 + i) * d + k0 + c] = x;
+    }
+    Lbuf[i * NB + c] = x;  // X_kk, zero outside the kb x kb lower triangle
   }
 }
 
@@ -254,32 +283,32 @@ hinv_panel(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb
 }
 
 // ----------------------------------------------------------- update step
-// 128x128 output tiles, K = kb <= 64. Each of the 4 waves owns a 64x64
-// quarter (4x4 MFMA 16x16 blocks). Operands are staged with 16-byte loads,
-// all issued before the first LDS store.
-constexpr int UT = 128;
-constexpr int UP = 66;   // pitch (doubles) of the [128][K] left operand
-constexpr int UQ = 132;  // pitch (doubles) of the [K][128] right operand
+// UT x UT output tiles (UT = 128 while the trailing matrix is large, 64 near
+// the end where a few big tiles would only add latency), K = kb <= 64. Each
+// of the 4 waves owns a (UT/2) x (UT/2) quarter of MFMA 16x16 blocks.
+// Operands are staged with every load issued before the first LDS store.
+constexpr int UP = 66;   // pitch (doubles) of the [UT][K] left operand
 
-// Stages a 128-row x 64-col fp64 block of M (rows r0.., cols k0..) into LDS,
+// Stages a UT-row x 64-col fp64 block of M (rows r0.., cols k0..) into LDS,
 // Ls[r][k] (transpose = false) or Ls[k][r] (transpose = true). Elements with
-// row >= rmax or col >= k0 + kmax read as zero. Every thread issues its 32
-// loads from clamped in-bounds addresses before storing anything.
-template <bool TRANSPOSE, typename Dst>
+// row >= rmax or col >= k0 + kmax read as zero; all loads use clamped
+// in-bounds addresses and are issued before anything is stored.
+template <int UT, bool TRANSPOSE, typename Dst>
 __device__ __forceinline__ void stage_block(Dst Ls, const double* __restrict__ M, int d, int r0, int rmax, int k0,
                                             int kmax) {
+  constexpr int PER = UT * 64 / 256;
   const int tid = threadIdx.x;
-  double v[32];
+  double v[PER];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const int e = tid + 256 * t;  // 8192 elements = 128 rows x 64 cols
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + 256 * t;
     const int r = e >> 6, k = e & 63;
     const bool ok = (r0 + r < rmax) && (k < kmax);
     v[t] = M[ok ? int64_t(r0 + r) * d + k0 + k : 0];
     v[t] = ok ? v[t] : 0.0;
   }
 #pragma unroll
-  for (int t = 0; t < 32; ++t) {
+  for (int t = 0; t < PER; ++t) {
     const int e = tid + 256 * t;
     const int r = e >> 6, k = e & 63;
     if (TRANSPOSE)
@@ -289,69 +318,78 @@ __device__ __forceinline__ void stage_block(Dst Ls, const double* __restrict__ M
   }
 }
 
-__device__ __forceinline__ void tile128_mma(const double (*Ls)[UP], const double (*Rs)[UQ], int K, doublex4 acc[4][4]) {
+template <int UT, int RQ>
+__device__ __forceinline__ void tileU_mma(const double (*Ls)[UP], const double (*Rs)[RQ], int K,
+                                          doublex4 acc[UT / 32][UT / 32]) {
+  constexpr int BL = UT / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   for (int k = 0; k < K; k += 4) {
-    double av[4], bv[4];
+    double av[BL], bv[BL];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) av[ii] = Ls[wr * 64 + ii * 16 + (lane & 15)][k + (lane >> 4)];
+    for (int ii = 0; ii < BL; ++ii) av[ii] = Ls[wr * (UT / 2) + ii * 16 + (lane & 15)][k + (lane >> 4)];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) bv[jj] = Rs[k + (lane >> 4)][wc * 64 + jj * 16 + (lane & 15)];
+    for (int jj = 0; jj < BL; ++jj) bv[jj] = Rs[k + (lane >> 4)][wc * (UT / 2) + jj * 16 + (lane & 15)];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int ii = 0; ii < BL; ++ii)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < BL; ++jj)
         acc[ii][jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii], bv[jj], acc[ii][jj], 0, 0, 0);
   }
 }
 
-// M[tile element] -= acc for the elements `keep` selects. All 64 loads are
+// M[tile element] -= acc for the elements `keep` selects. All loads are
 // issued unconditionally (masked-off ones read M[0]) before any store, so
 // the tile costs one memory round trip; only the stores are masked.
-template <typename Keep>
-__device__ __forceinline__ void rmw_sub(double* __restrict__ M, int d, int r0, int c0, doublex4 acc[4][4], Keep keep) {
+// v_mfma_f64_16x16x4f64 layout: lane l, register r -> row l/16 + 4r, col l%16.
+template <int UT, typename Keep>
+__device__ __forceinline__ void rmw_sub(double* __restrict__ M, int d, int r0, int c0,
+                                        doublex4 acc[UT / 32][UT / 32], Keep keep) {
+  constexpr int BL = UT / 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  double old[4][4][4];
+  double old[BL][BL][4];
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+  for (int ii = 0; ii < BL; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < BL; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int gi = r0 + wr * 64 + ii * 16 + (lane >> 4) + 4 * r;
-        const int gj = c0 + wc * 64 + jj * 16 + (lane & 15);
+        const int gi = r0 + wr * (UT / 2) + ii * 16 + (lane >> 4) + 4 * r;
+        const int gj = c0 + wc * (UT / 2) + jj * 16 + (lane & 15);
         old[ii][jj][r] = M[keep(gi, gj) ? int64_t(gi) * d + gj : 0];
       }
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+  for (int ii = 0; ii < BL; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < BL; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int gi = r0 + wr * 64 + ii * 16 + (lane >> 4) + 4 * r;
-        const int gj = c0 + wc * 64 + jj * 16 + (lane & 15);
+        const int gi = r0 + wr * (UT / 2) + ii * 16 + (lane >> 4) + 4 * r;
+        const int gj = c0 + wc * (UT / 2) + jj * 16 + (lane & 15);
         if (keep(gi, gj)) M[int64_t(gi) * d + gj] = old[ii][jj][r] - acc[ii][jj][r];
       }
 }
 
-// Blocks [0, nA): lower 128-tiles (ti >= tj) of the trailing matrix at k1:
+// Blocks [0, nA): lower UT-tiles (ti >= tj) of the trailing matrix at k1:
 //   A_ij -= L_i L_j^T.
-// Blocks [nA, nA + nT * nC): R[k1 + 128 ti, 128 tc] -= L_i X[k, 128 tc].
+// Blocks [nA, nA + nT * nC): R[k1 + UT ti, UT tc] -= L_i X[k, UT tc].
+template <int UT>
 __global__ void __launch_bounds__(256)
 hinv_update(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, int nT, int nC) {
+  constexpr int RQ = UT + 4;
+  constexpr int BL = UT / 32;
   __shared__ double Ls[UT][UP];
-  __shared__ double Rs[NB][UQ];
+  __shared__ double Rs[NB][RQ];
   const int k1 = k0 + kb;
   const int Kp = (kb + 3) & ~3;
   const int nA = nT * (nT + 1) / 2;
   int b = blockIdx.x;
-  doublex4 acc[4][4];
+  doublex4 acc[BL][BL];
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+  for (int ii = 0; ii < BL; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
+    for (int jj = 0; jj < BL; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
   if (b < nA) {
     int ti = 0;
     while (b > ti) {
@@ -360,39 +398,40 @@ hinv_update(double* __restrict__ A, double* __restrict__ R, int d, int k0, int k
     }
     const int tj = b;
     const int r0 = k1 + UT * ti, c0 = k1 + UT * tj;
-    stage_block<false>(Ls, A, d, r0, d, k0, kb);
-    stage_block<true>(Rs, A, d, c0, d, k0, kb);  // Rs[m][j] = L[c0 + j][k0 + m]
+    stage_block<UT, false>(Ls, A, d, r0, d, k0, kb);
+    stage_block<UT, true>(Rs, A, d, c0, d, k0, kb);  // Rs[m][j] = L[c0 + j][k0 + m]
     __syncthreads();
-    tile128_mma(Ls, Rs, Kp, acc);
-    rmw_sub(A, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj <= gi; });
+    tileU_mma<UT, RQ>(Ls, Rs, Kp, acc);
+    rmw_sub<UT>(A, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj <= gi; });
   } else {
     b -= nA;
     const int ti = b / nC, tc = b % nC;
     const int r0 = k1 + UT * ti, c0 = UT * tc;
-    stage_block<false>(Ls, A, d, r0, d, k0, kb);
+    stage_block<UT, false>(Ls, A, d, r0, d, k0, kb);
     {
       // Rs[m][c] = X[k0 + m][c0 + c]; X is lower triangular inside the
       // diagonal block (R's upper part is never written, so it is masked).
+      constexpr int PER = 64 * UT / 256;
       const int tid = threadIdx.x;
-      double v[32];
+      double v[PER];
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
-        const int e = tid + 256 * t;  // 64 rows x 128 cols
-        const int m = e >> 7, c = e & 127;
+      for (int t = 0; t < PER; ++t) {
+        const int e = tid + 256 * t;  // 64 rows x UT cols
+        const int m = e / UT, c = e % UT;
         const int g = c0 + c;
         const bool ok = m < kb && g < k1 && g <= k0 + m;
         v[t] = R[ok ? int64_t(k0 + m) * d + g : 0];
         v[t] = ok ? v[t] : 0.0;
       }
 #pragma unroll
-      for (int t = 0; t < 32; ++t) {
+      for (int t = 0; t < PER; ++t) {
         const int e = tid + 256 * t;
-        Rs[e >> 7][e & 127] = v[t];
+        Rs[e / UT][e % UT] = v[t];
       }
     }
     __syncthreads();
-    tile128_mma(Ls, Rs, Kp, acc);
-    rmw_sub(R, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj < k1; });
+    tileU_mma<UT, RQ>(Ls, Rs, Kp, acc);
+    rmw_sub<UT>(R, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj < k1; });
   }
 }
 
@@ -454,11 +493,19 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     if (nrow + ncol > 0)
       hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, di, k0, kb, w.Lbuf,
                          nrow);
-    const int nT = (di - k1 + UT - 1) / UT;
-    const int nC = (k1 + UT - 1) / UT;
-    const int nblk = nT * (nT + 1) / 2 + nT * nC;
-    if (nblk > 0)
-      hipLaunchKernelGGL(hinv_update, dim3(unsigned(nblk)), dim3(256), 0, s, w.A, w.R, di, k0, kb, nT, nC);
+    // 128-wide update tiles while they fill the GPU, 64-wide near the end.
+    const int rem = di - k1;
+    const int n128 = (rem + 127) / 128;
+    if (n128 * (n128 + 1) / 2 >= 256) {
+      const int nT = n128, nC = (k1 + 127) / 128;
+      const int nblk = nT * (nT + 1) / 2 + nT * nC;
+      hipLaunchKernelGGL(hinv_update<128>, dim3(unsigned(nblk)), dim3(256), 0, s, w.A, w.R, di, k0, kb, nT, nC);
+    } else {
+      const int nT = (rem + 63) / 64, nC = (k1 + 63) / 64;
+      const int nblk = nT * (nT + 1) / 2 + nT * nC;
+      if (nblk > 0)
+        hipLaunchKernelGGL(hinv_update<64>, dim3(unsigned(nblk)), dim3(256), 0, s, w.A, w.R, di, k0, kb, nT, nC);
+    }
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }
   hipLaunchKernelGGL(hinv_write_u, dim3(2048), dim3(256), 0, s, w.R, di, U);
