@@ -44,10 +44,13 @@ def upload_activations(cfg, torch, dev):
     from workload import activation_chunks
 
     X = torch.empty((cfg.n_tokens, cfg.d_col), dtype=getattr(torch, cfg.x_dtype), device=dev)
-    t = 0
+    t, t0, shown = 0, time.perf_counter(), time.perf_counter()
     for ch in activation_chunks(cfg, threads=min(16, os.cpu_count() or 8)):
         X[t : t + ch.shape[0]].copy_(torch.from_numpy(ch))
         t += ch.shape[0]
+        if time.perf_counter() - shown > 20:
+            shown = time.perf_counter()
+            log(f"bench: {t} of {cfg.n_tokens} tokens generated and uploaded ({shown - t0:.0f} s)")
     return X
 
 

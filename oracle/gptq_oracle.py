@@ -146,7 +146,7 @@ def prepare_hinv(H: np.ndarray, damp: float):
 # --------------------------------------------------------------------------
 # Quantizer
 # --------------------------------------------------------------------------
-def group_params(x: np.ndarray, bits: int, decide=F64):
+def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False):
     """Per-row min-max scale and integer zero of a group of columns.
 
     aiqz.cc, section 分组方案: scale = (max - min)/(2^bits - 1) and the zero
@@ -158,6 +158,8 @@ def group_params(x: np.ndarray, bits: int, decide=F64):
     ``x`` is [rows, cols]. Returns (s, z) as float64 arrays [rows]; z holds
     integers. ``decide`` is the precision of the division and rounding
     that fixes z (float64, or float32 to match a float32 implementation).
+    With ``with_margin`` it also returns how far -xmin/s lay from the nearest
+    rounding boundary, in grid steps (0 = an exact tie, 0.5 = an integer).
     """
     maxq = (1 << bits) - 1
     xmin = np.minimum(np.min(x, axis=1), 0.0)
@@ -167,22 +169,33 @@ def group_params(x: np.ndarray, bits: int, decide=F64):
     xmax = np.where(dead, 1.0, xmax)
     if decide == F64:
         s = (xmax - xmin) / maxq
-        z = np.rint(-xmin / s)
+        t = -xmin / s
     else:
         s32 = (xmax.astype(decide) - xmin.astype(decide)) / decide(maxq)
-        z = np.rint((-xmin.astype(decide)) / s32).astype(F64)
+        t = ((-xmin.astype(decide)) / s32).astype(F64)
         s = s32.astype(F64)
+    z = np.rint(t)
+    if with_margin:
+        return s.astype(F64), z.astype(F64), 0.5 - np.abs(t - z)
     return s.astype(F64), z.astype(F64)
 
 
-def quantize_codes(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decide=F64) -> np.ndarray:
-    """code = clamp(rint(w/s) + z, 0, 2^b - 1) (astro-blog survey, 1.2)."""
+def quantize_codes(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decide=F64, with_margin: bool = False):
+    """code = clamp(rint(w/s) + z, 0, 2^b - 1) (astro-blog survey, 1.2).
+
+    With ``with_margin`` it also returns how far w/s lay from the nearest
+    rounding boundary, in grid steps (0 = an exact tie).
+    """
     maxq = (1 << bits) - 1
     if decide == F64:
-        q = np.rint(w / s)
+        t = w / s
     else:
-        q = np.rint(w.astype(decide) / s.astype(decide)).astype(F64)
-    return np.clip(q + z, 0, maxq)
+        t = (w.astype(decide) / s.astype(decide)).astype(F64)
+    q = np.rint(t)
+    c = np.clip(q + z, 0, maxq)
+    if with_margin:
+        return c, 0.5 - np.abs(t - q)
+    return c
 
 
 def rtn(W: np.ndarray, bits: int, group_size: int):
@@ -245,7 +258,11 @@ def quantize_layer(
     W is [d_row, d_col] (any float dtype; upcast exactly to float64). U is
     [d_col, d_col] upper triangular. Returns a dict with codes (uint8),
     scales, zeros (float64, integer-valued), Wq (the dequantized weights),
-    row_loss and loss (sum over columns of err^2 / (2 U_qq^2)), and packed.
+    row_loss and loss (sum over columns of err^2 / (2 U_qq^2)), packed, and
+    two diagnostics of how close each decision came to a tie:
+    code_margin [d_row, d_col] (distance of w/s from the nearest rounding
+    boundary, in grid steps) and zero_margin [d_row, n_groups] (the same for
+    -xmin/s when the zero point was chosen).
     ``decide`` is the precision in which each code is decided (float64 by
     default; float32 reproduces the decision of a float32 implementation
     given the same inputs).
@@ -268,10 +285,12 @@ def quantize_layer(
     zeros = np.zeros((d_row, n_groups))
     Wq = np.zeros((d_row, d_col))
     row_loss = np.zeros(d_row)
+    code_margin = np.zeros((d_row, d_col))
+    zero_margin = np.zeros((d_row, n_groups))
 
     if group_size == -1 and d_col:
-        s, z = group_params(W, bits, decide)
-        scales[:, 0], zeros[:, 0] = s, z
+        s, z, zm = group_params(W, bits, decide, with_margin=True)
+        scales[:, 0], zeros[:, 0], zero_margin[:, 0] = s, z, zm
 
     for i1 in range(0, d_col, block):
         i2 = min(i1 + block, d_col)
@@ -279,10 +298,10 @@ def quantize_layer(
         for q in range(i1, i2):
             if group_size != -1 and q % group_size == 0:
                 k = q // group_size
-                s, z = group_params(W[:, q : min(q + group_size, d_col)], bits, decide)
-                scales[:, k], zeros[:, k] = s, z
+                s, z, zm = group_params(W[:, q : min(q + group_size, d_col)], bits, decide, with_margin=True)
+                scales[:, k], zeros[:, k], zero_margin[:, k] = s, z, zm
             w = W[:, q]
-            c = quantize_codes(w, s, z, bits, decide)
+            c, code_margin[:, q] = quantize_codes(w, s, z, bits, decide, with_margin=True)
             what = s * (c - z)
             err = w - what
             d = U[q, q]
@@ -303,6 +322,8 @@ def quantize_layer(
         row_loss=row_loss,
         loss=float(np.sum(row_loss)),
         packed=pack(codes, bits),
+        code_margin=code_margin,
+        zero_margin=zero_margin,
     )
 
 

@@ -2,9 +2,10 @@
 
 Inputs always flow from the seeded generators or the oracle to the GPU; no
 value produced by the HIP path is fed back into the oracle. Tolerances:
-H within 1e-4 relative Frobenius error; codes equal on >= 99.9% of entries
-with every mismatch within one step; scales within 1e-3 relative error;
-loss within 1%; packed words bit-exact for the same codes.
+H within 1e-4 relative Frobenius error; codes equal on >= 99.9% of entries,
+each row's first mismatch one step away at a decision the oracle took within
+1e-3 grid steps of a tie; scales within 1e-3 relative error up to each row's
+first mismatch; loss within 1%; packed words bit-exact for the same codes.
 """
 
 import numpy as np
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 import oracle.gptq_oracle as O
-from workload import CONFIGS, activations, weights
+from workload import CONFIGS, activation_chunks, activations, weights
 from workload.synth import small
 
 pytestmark = pytest.mark.gpu
@@ -33,7 +34,7 @@ def gpu_tensor(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def check_quant(q, ref, bits, rows=None):
+def check_quant(q, ref, bits, rows=None, tie=1e-3):
     codes = q.codes.cpu().numpy()
     scales = q.scales.cpu().numpy()
     zeros = q.zeros.cpu().numpy()
@@ -43,22 +44,34 @@ def check_quant(q, ref, bits, rows=None):
         codes, scales, zeros, packed, row_loss = codes[rows], scales[rows], zeros[rows], packed[rows], row_loss[rows]
     diff = codes.astype(int) - ref["codes"].astype(int)
     match = float(np.mean(diff == 0))
-    assert match >= 0.999, f"codes match {match}"
-    assert np.max(np.abs(diff)) <= 1
-    # Scales are unique only while a row's history is identical: after a code
-    # decided differently at a near-tie (fp32 vs fp64 accumulation), both
-    # continuations are valid and that row's later groups see slightly
-    # different compensated values. Compare groups up to each row's first
-    # differing code to 1e-3; check the rest stay close and valid.
+    assert int(codes.max()) <= (1 << bits) - 1
+    # A row's results are unique only while its history is identical. Its
+    # first differing code must be a decision the oracle itself took at a
+    # near-tie, either the code's own rounding or its group's zero point, and
+    # must differ by one step. After that both continuations are valid: the
+    # row's later groups see slightly different compensated values. Scales
+    # (to 1e-3) and zeros (exactly) must agree up to each row's first
+    # differing code; after it they must stay valid and within 5e-2.
     d_col = codes.shape[1]
     ng = scales.shape[1]
     g = d_col if ng == 1 else -(-d_col // ng)
     first = np.where((diff != 0).any(axis=1), np.argmax(diff != 0, axis=1), d_col)
-    same = (np.arange(ng)[None, :] * g) <= first[:, None]
+    for r in np.nonzero(first < d_col)[0]:
+        c = first[r]
+        k = c // g
+        assert abs(diff[r, c]) == 1, (r, c, diff[r, c])
+        near_tie = ref["code_margin"][r, c] < tie or (
+            zeros[r, k] != ref["zeros"][r, k] and ref["zero_margin"][r, k] < tie
+        )
+        assert near_tie, (r, c, ref["code_margin"][r, c], ref["zero_margin"][r, k])
+    n_div = int(np.sum(first < d_col))
+    say(f"  codes match {match:.6f}; rows with a near-tie flip {n_div}/{len(first)}; "
+        f"entries before each row's first flip {float(np.mean(np.minimum(first, d_col))) / d_col:.4f}")
+    assert match >= 0.999, f"codes match {match}"
+    same = (np.arange(ng)[None, :] * g) < first[:, None]
     assert np.allclose(scales[same], ref["scales"][same], rtol=1e-3, atol=0)
     assert np.all(zeros[same] == ref["zeros"][same])
     assert np.all(scales > 0) and np.allclose(scales, ref["scales"], rtol=5e-2)
-    assert np.mean(same) >= 0.99
     # packing of the GPU's own codes is bit-exact
     assert np.array_equal(packed, O.pack(codes, bits))
     lref = float(np.sum(ref["row_loss"]))
@@ -293,11 +306,16 @@ def test_chain_full_size_attention_layer(gpu):
     say("full-size", cfg.name)
     Xd = torch.empty((cfg.n_tokens, cfg.d_col), dtype=torch.float16, device=DEV)
     t = 0
-    Href = np.zeros((cfg.d_col, cfg.d_col))
-    for ch in __import__("workload").activation_chunks(cfg, threads=8):
-        Xd[t : t + ch.shape[0]] = torch.from_numpy(ch).to(DEV)
-        Href += 2.0 * (ch.astype(np.float64).T @ ch.astype(np.float64))
-        t += ch.shape[0]
+
+    def uploaded_chunks():
+        nonlocal t
+        for ch in activation_chunks(cfg, threads=8):
+            Xd[t : t + ch.shape[0]] = torch.from_numpy(ch).to(DEV)
+            t += ch.shape[0]
+            yield ch
+
+    Href = O.hessian(uploaded_chunks())
+    assert t == cfg.n_tokens
     W = weights(cfg)
     H, hv, q = run_chain(gpu, cfg, Xd, W)
     e = rel_fro(H.cpu().numpy(), Href)
@@ -306,7 +324,7 @@ def test_chain_full_size_attention_layer(gpu):
     U, _ = O.prepare_hinv(Href, cfg.damp)
     eu = rel_fro(hv.U.cpu().numpy(), U)
     say("U rel fro", eu)
-    assert int(hv.info.item()) == 0 and eu < 1e-2
+    assert int(hv.info.item()) == 0 and eu < 1e-5
     rows = np.sort(np.random.default_rng(0).choice(cfg.d_row, 256, replace=False))
     ref = O.quantize_layer(W[rows], U, cfg.bits, cfg.group_size, cfg.block, decide=np.float32)
     m = check_quant(q, ref, cfg.bits, rows=rows)

@@ -1,0 +1,111 @@
+"""Full-size parity for every layer configuration, in the launch configuration
+the benchmark times (needs an MI355X).
+
+* Hessian: the GPU computes H from the full activation matrix and the oracle
+  computes the same H in float64, chunk by chunk; they are compared in full.
+* Factor: both sides factor that oracle Hessian, rounded to fp32 as the
+  library receives it, and are compared in full.
+* Sweep: the GPU quantizes the whole weight matrix with the oracle's factor.
+  The oracle sweeps a seeded sample of 256 rows; rows are independent given U.
+
+No value from the HIP path is fed to the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gptq_oracle as O
+from tests.test_gpu_parity import DEV, check_quant, gpu_tensor, rel_fro, say
+from workload import CONFIGS, activation_chunks, weights
+
+pytestmark = pytest.mark.gpu
+
+FULL_SIZE = [
+    "attn_proj_4096x4096_4bit_g128",
+    "mlp_up_11008x4096_4bit_g128",
+    "attn_proj_4096x4096_3bit_g128",
+    "attn_proj_4096x4096_3bit_rowwise",
+    "mlp_down_4096x11008_4bit_g128",
+    "opt175b_12288x12288_3bit_g128",
+    "opt175b_49152x12288_3bit_g128",
+]
+N_SAMPLE_ROWS = 256
+
+# Per activation recipe and damping: the oracle's U in fp32.
+_cache = {}
+
+
+def x_key(cfg):
+    return (cfg.seed, cfg.n_tokens, cfg.d_col, cfg.x_dtype, cfg.outlier_frac, cfg.outlier_factor, cfg.token_scale)
+
+
+def hessian_stage(gpu, cfg):
+    """GPU H of the full X against the oracle's; returns the oracle's H."""
+    Xd = torch.empty((cfg.n_tokens, cfg.d_col), dtype=getattr(torch, cfg.x_dtype), device=DEV)
+    t = 0
+
+    def uploaded_chunks():
+        nonlocal t
+        for ch in activation_chunks(cfg, threads=16):
+            Xd[t : t + ch.shape[0]].copy_(torch.from_numpy(ch))
+            t += ch.shape[0]
+            yield ch
+
+    H_ref = O.hessian(uploaded_chunks())
+    assert t == cfg.n_tokens
+    H = gpu.gptq_hessian_accumulate(Xd)
+    torch.cuda.synchronize()
+    del Xd
+    Hc = H.cpu().numpy()
+    del H
+    torch.cuda.empty_cache()
+    e = rel_fro(Hc, H_ref)
+    say(f"{cfg.name}: H (d={cfg.d_col}, {cfg.n_tokens} tokens) rel fro {e:.3g}")
+    assert e < 1e-4
+    assert np.array_equal(Hc, Hc.T)  # both triangles written, identical
+    return H_ref
+
+
+def factor_stage(gpu, cfg, Hf):
+    H32 = Hf.astype(np.float32)
+    U_ref, lam = O.prepare_hinv(H32.astype(np.float64), cfg.damp)
+    hv = gpu.gptq_prepare_hinv(gpu_tensor(H32), cfg.damp)
+    torch.cuda.synchronize()
+    assert int(hv.info.item()) == 0
+    assert abs(float(hv.lam.item()) - lam) <= 1e-6 * lam
+    U = hv.U.cpu().numpy()
+    e = rel_fro(U, U_ref)
+    say(f"{cfg.name}: U (d={cfg.d_col}) rel fro {e:.3g}")
+    assert e < 1e-6
+    assert np.all(np.tril(U, -1) == 0)
+    return U_ref.astype(np.float32)
+
+
+def prepared(gpu, cfg):
+    key = x_key(cfg) + (cfg.damp,)
+    if key not in _cache:
+        Hf = hessian_stage(gpu, cfg)
+        _cache[key] = factor_stage(gpu, cfg, Hf)
+    return _cache[key]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_full_size_layer(gpu, name):
+    cfg = CONFIGS[name]
+    say(f"full-size {name}: W {cfg.d_row}x{cfg.d_col}, X {cfg.n_tokens}x{cfg.d_col}, {cfg.bits}-bit g{cfg.group_size}")
+    U32 = prepared(gpu, cfg)
+    W = weights(cfg)
+    q = gpu.gptq_quantize_layer(gpu_tensor(W), gpu_tensor(U32), cfg.bits, cfg.group_size, cfg.block)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(7).choice(cfg.d_row, N_SAMPLE_ROWS, replace=False))
+    rows[-1] = cfg.d_row - 1
+    rows = np.unique(rows)
+    ref = O.quantize_layer(W[rows], U32.astype(np.float64), cfg.bits, cfg.group_size, cfg.block, decide=np.float32)
+    m = check_quant(q, ref, cfg.bits, rows=rows)
+    say(f"{name}: sampled rows {len(rows)}, codes match {m:.6f}")
+    # outputs of every row are on the grid: zeros within range, scales positive
+    zeros = q.zeros.cpu().numpy()
+    assert zeros.min() >= 0 and zeros.max() <= (1 << cfg.bits) - 1
+    assert bool(torch.all(q.scales > 0)) and bool(torch.isfinite(q.loss))

@@ -128,6 +128,28 @@ def test_identity_hessian_reduces_to_rtn(bits, group):
     assert out["loss"] == pytest.approx(0.5 * (1 + lam) * np.sum((W - what) ** 2), rel=1e-12)
 
 
+def test_decision_margins():
+    # w/s = 2.5 (exact tie), 3.0, 2.4, -0.75 -> distance to the nearest
+    # rounding boundary 0, 0.5, 0.1, 0.25 grid steps
+    s = np.full(4, 0.125)
+    c, m = O.quantize_codes(np.array([2.5, 3.0, 2.4, -0.75]) * 0.125, s, np.zeros(4), 4, with_margin=True)
+    assert c.tolist() == [2, 3, 2, 0]
+    assert m == pytest.approx([0.0, 0.5, 0.1, 0.25], abs=1e-12)
+    # range [-0.3, 0.9] at 2 bits: s = 0.4, -xmin/s = 0.75 -> z = 1, margin 0.25
+    s, z, zm = O.group_params(np.array([[-0.3, 0.9]]), 2, with_margin=True)
+    assert s[0] == pytest.approx(0.4, rel=1e-15) and z[0] == 1 and zm[0] == pytest.approx(0.25, abs=1e-12)
+    # with H = I nothing is compensated: each code's margin is that of the
+    # weight itself on the round-to-nearest grid
+    W = 0.02 * rng(5).standard_normal((5, 32))
+    U, _ = O.prepare_hinv(np.eye(32), 0.0)
+    out = O.quantize_layer(W, U, 3, 16, block=8)
+    sc = np.repeat(out["scales"], 16, axis=1)
+    t = W / sc
+    assert out["code_margin"] == pytest.approx(0.5 - np.abs(t - np.rint(t)), abs=1e-12)
+    assert out["zero_margin"].shape == (5, 2)
+    assert np.all((out["code_margin"] >= 0) & (out["code_margin"] <= 0.5))
+
+
 @pytest.mark.parametrize("bits,group,blocks", [(4, -1, [1, 2, 3, 5, 16, 128, 64]), (3, 8, [1, 2, 4, 8, 16, 32, 64]), (2, 32, [1, 4, 8, 32, 64])])
 def test_blocked_equals_unblocked(bits, group, blocks):
     _, W, _, U, _ = sweep_case(6, 64, 400, 11)
