@@ -13,17 +13,23 @@
 // J L^-1 J. The Cholesky factor with positive diagonal is unique, so this is
 // the factor of H_d^-1 itself.
 //
-// L and X = L^-1 are computed together by a right-looking blocked
-// elimination in fp64 (panel width 64):
-//   diag   (1 workgroup): L_kk = chol(A_kk) and X_kk = L_kk^-1 in LDS; a
-//          pivot that is not positive sets `info`.
-//   panel  (many):        L_ik = A_ik X_kk^T            for row blocks i > k
-//                         X[k, :k] = X_kk R[k, :k]      (block row k of X)
-//   update (many):        A_ij -= L_ik L_jk^T           (trailing lower part)
-//                         R[i, :k+1] -= L_ik X[k, :k+1] (rows i > k)
-// R starts as the identity; block row i of R becomes block row i of X once
-// its own panel step runs. Each step's products are 64x64 tiles on the fp64
-// MFMA (v_mfma_f64_16x16x4f64).
+// L and X = L^-1 are computed together in fp64, 64 columns at a time, with
+// the trailing update applied once per 128-column super-panel S = [s0, s1):
+//   diag  (1 workgroup): A_kk -= L_kS' L_kS'^T over the super-panel's earlier
+//         blocks S' (left-looking), then X_kk = chol(A_kk)^-1; a pivot that
+//         is not positive sets `info`.
+//   panel (many):  row blocks i > k:  L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T,
+//                                     kept column-major in the panel buffer LT
+//                  col blocks c < k:  X_kc = X_kk (R_kc - L_kS' X_S'c)
+//   trail (many, once per super-panel, K = 128):
+//                  A_ij -= L_iS L_jS^T   for i >= j >= s1 (lower tiles)
+//                  R_ic -= L_iS X_Sc     for i >= s1, c < s1
+// R starts as the identity; block row k of R becomes block row k of X once
+// its diag and panel steps have run. All products use the fp64 MFMA
+// (v_mfma_f64_16x16x4f64). The trailing update, which holds almost all of
+// the flops, reads the trailing matrix once per 128 columns instead of once
+// per 64, and reads its operands straight from L2 with 16 independent MFMA
+// chains per wave.
 #include <utility>
 
 #include "gptq_common.h"
@@ -31,8 +37,20 @@
 namespace gptq {
 namespace {
 
-constexpr int NB = 64;   // panel width
-constexpr int LP = 68;   // LDS pitch (doubles) of 64-wide operand tiles
+constexpr int NB = 64;   // block (diagonal factorization) width
+constexpr int KS = 128;  // super-panel width
+
+template <int Q, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (Q < N) {
+    f(std::integral_constant<int, Q>{});
+    static_for<Q + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ doublex4 mfma64(double a, double b, doublex4 c) {
+  return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
 
 // ---------------------------------------------------------------- setup
 __global__ void __launch_bounds__(256)
@@ -56,11 +74,10 @@ hinv_lambda(const float* __restrict__ H, int d, double damp, double* __restrict_
 }
 
 // A[i][j] = H[d-1-j][d-1-i] + lambda [i == j] for j <= i (reads H's lower
-// triangle, which is the reversed matrix's lower triangle by symmetry);
-// R = identity on and below the diagonal. One 32x32 lower block per group.
+// triangle, which is the reversed matrix's lower triangle by symmetry).
+// One 32x32 lower block per workgroup.
 __global__ void __launch_bounds__(256)
-hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, double* __restrict__ A,
-           double* __restrict__ R) {
+hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, double* __restrict__ A) {
   __shared__ float t[32][33];
   int b = blockIdx.x, bi = 0;
   while (b > bi) {
@@ -80,359 +97,417 @@ hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, d
     const int ii = e >> 5, jj = e & 31;
     const int i = i0 + ii, j = j0 + jj;
     if (i >= d || j >= d || j > i) continue;
-    const int64_t o = int64_t(i) * d + j;
-    A[o] = double(t[jj][ii]) + (i == j ? l : 0.0);
-    R[o] = (i == j) ? 1.0 : 0.0;
+    A[int64_t(i) * d + j] = double(t[jj][ii]) + (i == j ? l : 0.0);
   }
+}
+
+// R = identity (both triangles: the panel and trailing products read R's
+// upper part inside finished block rows and rely on it being zero).
+__global__ void __launch_bounds__(256) hinv_eye(double* __restrict__ R, int d) {
+  const int64_t n = int64_t(d) * d;
+  for (int64_t e = (blockIdx.x * int64_t(256) + threadIdx.x) * 2; e < n; e += int64_t(gridDim.x) * 512) {
+    const int64_t i0 = e / d, j0 = e % d;
+    R[e] = (i0 == j0) ? 1.0 : 0.0;
+    if (e + 1 < n) {
+      const int64_t i1 = (e + 1) / d, j1 = (e + 1) % d;
+      R[e + 1] = (i1 == j1) ? 1.0 : 0.0;
+    }
+  }
+}
+
+// ------------------------------------------------------------ MFMA helpers
+// v_mfma_f64_16x16x4f64 operands: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; result: lane l, register r holds row l / 16 + 4 r,
+// column l % 16 of the 16x16 block.
+
+// acc[t] += Aop * Bop for NBLK 16x16 blocks over k in [0, K), K a multiple
+// of 4, with both operands in LDS: Aop(i, k) = As[k * pa + i] ("k-major",
+// rows contiguous) or As[i * pa + k]; Bop(k, j) = Bs[k * pb + j].
+// Block t covers rows ri[t] .. + 16, columns cj[t] .. + 16.
+template <int NBLK, bool A_KMAJOR>
+__device__ __forceinline__ void blocks_mma(doublex4 (&acc)[NBLK], const double* As, int pa, const double* Bs, int pb,
+                                           const int (&ri)[NBLK], const int (&cj)[NBLK], int K) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lk = lane >> 4;
+  for (int k = 0; k < K; k += 4) {
+#pragma unroll
+    for (int t = 0; t < NBLK; ++t) {
+      const double a = A_KMAJOR ? As[(k + lk) * pa + ri[t] + lr] : As[(ri[t] + lr) * pa + k + lk];
+      const double b = Bs[(k + lk) * pb + cj[t] + lr];
+      acc[t] = mfma64(a, b, acc[t]);
+    }
+  }
+}
+
+// f(row, col, value) for every accumulator element of the blocks.
+template <int NBLK, typename F>
+__device__ __forceinline__ void blocks_for_each(doublex4 (&acc)[NBLK], const int (&ri)[NBLK], const int (&cj)[NBLK],
+                                                F f) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < NBLK; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f(ri[t] + (lane >> 4) + 4 * r, cj[t] + (lane & 15), acc[t][r]);
+}
+
+template <int NBLK>
+__device__ __forceinline__ void zero(doublex4 (&acc)[NBLK]) {
+#pragma unroll
+  for (int t = 0; t < NBLK; ++t) acc[t] = doublex4{0, 0, 0, 0};
+}
+
+// 1/x to within an ulp: hardware estimate plus two Newton steps.
+__device__ __forceinline__ double recip(double x) {
+  double r = __builtin_amdgcn_rcp(x);
+  r = fma(r, fma(-x, r, 1.0), r);
+  r = fma(r, fma(-x, r, 1.0), r);
+  return r;
 }
 
 // ------------------------------------------------------------ diag block
-// Factor the kb x kb diagonal block at k0 and invert its factor. Schur form:
-// step j eliminates column j with multipliers m_i = a_ij / a_jj, applied both
-// to the trailing block (a_ic -= m_i a_cj, c in (j, i]) and to the unit-lower
-// inverse Y (y_ic -= m_i y_jc, c <= j). Then L_ij = a_ij / sqrt(a_jj) and
-// L^-1_ic = y_ic / sqrt(a_ii). Rows and columns past kb act as identity.
+// Factor the kb x kb diagonal block at k0, after the left-looking update
+// A_kk -= L_kS' L_kS'^T over the kl earlier columns of the super-panel, and
+// invert its factor.
 //
-// Thread t owns row i = t / 4, columns c = t % 4 + 4 m (m < 16) of both a and
-// y, in registers, for all 64 (fully unrolled) steps. Step j only exchanges
-// column j of a and row j of y through LDS (double buffered: one barrier).
-template <int Q, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (Q < N) {
-    f(std::integral_constant<int, Q>{});
-    static_for<Q + 1, N>(f);
-  }
-}
-
+// Gauss-Jordan form on one symmetric 64x64 array v: step j eliminates
+// column j with multipliers m_i = v_ij / v_jj (i > j). Columns c > j still
+// hold the Schur complement (v_ic -= m_i v_jc); columns c < j hold the
+// unit-lower inverse Y (v_ic -= m_i y_jc); column j itself becomes Y's
+// column j (-m_i, and 1 on the diagonal). Row j of v therefore carries
+// everything step j needs: y_jc left of the diagonal, the pivot, and the
+// Schur row, which equals the Schur column by symmetry (m_i = v_ji / v_jj).
+// After 64 steps X_kk = L^-1 has X_ic = y_ic / sqrt(pivot_i). Rows and
+// columns past kb act as identity.
+//
+// Thread t owns the 4x4 block rows 4 (t / 16) .., columns 4 (t % 16) .. in
+// registers for all 64 steps; the 16 threads that hold row j (one quarter of
+// one wave) write it to LDS, double buffered, one barrier per step.
 __global__ void __launch_bounds__(256)
-hinv_diag(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, double* __restrict__ Lbuf,
-          int32_t* __restrict__ info) {
-  __shared__ double acol[2][NB];
-  __shared__ double yrow[2][NB];
-  __shared__ double dg[NB];
-  const int tid = threadIdx.x;
-  const int i_ = tid >> 2, c0_ = tid & 3;
-  double av[NB / 4], yv[NB / 4];
-  const int i = i_, c0 = c0_;
+hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, int k0, int kb,
+          int kl, double* __restrict__ Xkk, double* __restrict__ XkkT, int32_t* __restrict__ info) {
+  __shared__ double Ls[KS - NB][NB];  // Ls[m][i] = L[k0 + i][s0 + m]
+  __shared__ double T[NB][NB + 1];
+  __shared__ __attribute__((aligned(16))) double bv[2][NB];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  // issue every load first: the diagonal block and the panel rows L_kS'
+  constexpr int PER = NB * NB / 256;
+  double av[PER], lv[PER];
 #pragma unroll
-  for (int t = 0; t < NB / 4; ++t) {
-    const int c = c0 + 4 * t;
-    const bool in = i < kb && c <= i;
-    const double v = A[in ? int64_t(k0 + i) * d + k0 + c : int64_t(k0) * d + k0];
-    av[t] = in ? v : (i == c ? 1.0 : 0.0);
-    yv[t] = (i == c) ? 1.0 : 0.0;
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
+    const bool ok = i < kb && j <= i;
+    av[t] = A[ok ? int64_t(k0 + i) * d + k0 + j : int64_t(k0) * d + k0];
+    const int m = e >> 6, c = e & 63;  // m < kl, c < 64
+    const bool lok = m < kl;
+    lv[t] = LT[lok ? int64_t(m) * d + k0 + (c < kb ? c : kb - 1) : 0];
   }
-  static_for<0, NB>([&](auto jc) {
-    constexpr int j = decltype(jc)::value;
-    constexpr int b = j & 1;
-    // Fresh copies of the lane indices each step, so the compiler computes
-    // this step's comparisons here instead of keeping all 64 steps' live.
-    int i = i_, c0 = c0_;
-    asm volatile("" : "+v"(i), "+v"(c0));
-    if (c0 == (j & 3)) acol[b][i] = av[j >> 2];  // column j of a (all rows)
-    if (i == j) {
 #pragma unroll
-      for (int t = 0; t < NB / 4; ++t) yrow[b][c0 + 4 * t] = yv[t];  // row j of y
-    }
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
+    T[i][j] = (i < kb && j <= i) ? av[t] : 0.0;
+    if ((e >> 6) < kl) Ls[e >> 6][e & 63] = lv[t];
+  }
+  __syncthreads();
+  if (kl > 0) {
+    // wave w: rows 16 w .. + 16, all four column blocks
+    doublex4 acc[4];
+    zero(acc);
+    const int ri[4] = {16 * wave, 16 * wave, 16 * wave, 16 * wave};
+    const int cj[4] = {0, 16, 32, 48};
+    blocks_mma<4, true>(acc, &Ls[0][0], NB, &Ls[0][0], NB, ri, cj, kl);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { T[i][j] -= s; });
     __syncthreads();
-    const double piv = acol[b][j];
-    if (tid == 0) {
-      dg[j] = piv;
-      if (j < kb && !(piv > 0.0)) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + j)));
+  }
+  const int rb_ = 4 * (tid >> 4), cb_ = 4 * (tid & 15);
+  double v[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = rb_ + r, j = cb_ + c;
+      const bool in = i < kb && j < kb;
+      const double t = T[i > j ? i : j][i > j ? j : i];
+      v[r][c] = in ? t : (i == j ? 1.0 : 0.0);
     }
-    const double m = i > j ? acol[b][i] / piv : 0.0;
-    static_for<0, NB / 4>([&](auto tc) {
-      constexpr int t = decltype(tc)::value;
-      const int c = c0 + 4 * t;
-      if constexpr (4 * t > j) {
-        av[t] = fma(-m, acol[b][c], av[t]);
-      } else if constexpr (4 * t + 3 <= j) {
-        yv[t] = fma(-m, yrow[b][c], yv[t]);
-      } else {
-        const bool up = c > j;
-        const double o = up ? acol[b][c] : yrow[b][c];
-        const double nv = fma(-m, o, up ? av[t] : yv[t]);
-        av[t] = up ? nv : av[t];
-        yv[t] = up ? yv[t] : nv;
+  double dr[4] = {1.0, 1.0, 1.0, 1.0};
+  // A loop of 16 iterations of 4 unrolled steps: the body stays small
+  // enough to run from the instruction cache (each launch runs it once).
+#pragma nounroll
+  for (int jb = 0; jb < NB; jb += 4) {
+    static_for<0, 4>([&](auto jc) {
+      constexpr int jq = decltype(jc)::value;
+      constexpr int b = jq & 1;
+      const int j = jb + jq;
+      if (rb_ == jb) {
+        *reinterpret_cast<double2*>(&bv[b][cb_]) = double2{v[jq][0], v[jq][1]};
+        *reinterpret_cast<double2*>(&bv[b][cb_ + 2]) = double2{v[jq][2], v[jq][3]};
+      }
+      __syncthreads();
+      const double piv = bv[b][j];
+      const double2 r01 = *reinterpret_cast<const double2*>(&bv[b][rb_]);
+      const double2 r23 = *reinterpret_cast<const double2*>(&bv[b][rb_ + 2]);
+      const double2 c01 = *reinterpret_cast<const double2*>(&bv[b][cb_]);
+      const double2 c23 = *reinterpret_cast<const double2*>(&bv[b][cb_ + 2]);
+      const bool own_row = rb_ == jb, own_col = cb_ == jb;
+      dr[jq] = own_row ? piv : dr[jq];
+      const double rp = recip(piv);
+      const double brow[4] = {r01.x, r01.y, r23.x, r23.y};
+      const double bcol[4] = {c01.x, c01.y, c23.x, c23.y};
+      double m[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = (rb_ + r > j) ? brow[r] * rp : 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const double nv = fma(-m[r], bcol[c], v[r][c]);
+          if (c == jq) {
+            const double ycol = (r == jq && own_row) ? 1.0 : -m[r];
+            v[r][c] = own_col ? ycol : nv;
+          } else {
+            v[r][c] = nv;
+          }
+        }
       }
     });
-    // Materialize this step's updates now (otherwise the compiler defers the
-    // fma chains and keeps every step's operands live).
-#pragma unroll
-    for (int t = 0; t < NB / 4; ++t) asm volatile("" : "+v"(av[t]), "+v"(yv[t]));
-  });
+  }
+  // The first pivot that is not positive (NaN included) sets `info` to one
+  // plus its index in H.
+  __shared__ int bad;
+  if (tid == 0) bad = NB;
   __syncthreads();
+  if (cb_ == 0) {
 #pragma unroll
-  for (int t = 0; t < NB / 4; ++t) {
-    const int c = c0 + 4 * t;
-    double x = 0.0;
-    if (i < kb && c <= i) {
-      const double sc = sqrt(dg[c]), si = sqrt(dg[i]);
-      const double l = (c == i) ? si : av[t] / sc;
-      x = yv[t] / si;
-      A[int64_t(k0 + i) * d + k0 + c] = l;
-      R[int64_t(k0 + i) * d + k0 + c] = x;
+    for (int r = 0; r < 4; ++r)
+      if (rb_ + r < kb && !(dr[r] > 0.0)) atomicMin(&bad, rb_ + r);
+  }
+  __syncthreads();
+  if (tid == 0 && bad < NB) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + bad)));
+  // X_kk = D^-1/2 Y: write it row-major and transposed for the panel step,
+  // and into R's diagonal block (zeros above the diagonal).
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = rb_ + r;
+    const double si = 1.0 / sqrt(dr[r]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = cb_ + c;
+      const double x = (i < kb && j <= i) ? v[r][c] * si : 0.0;
+      Xkk[i * NB + j] = x;
+      XkkT[j * NB + i] = x;
+      if (i < kb && j < kb) R[int64_t(k0 + i) * d + k0 + j] = x;
     }
-    Lbuf[i * NB + c] = x;  // X_kk, zero outside the kb x kb lower triangle
   }
-}
-
-// ------------------------------------------------------ 64x64 tile products
-// Each of the 4 waves owns a 32x32 quarter (2x2 MFMA 16x16 blocks).
-// Ls[i][k] (pitch LP) is the left operand, Rs[k][j] (pitch LP) the right one;
-// K is a multiple of 4 (zero padded).
-__device__ __forceinline__ void tile_mma(const double (*Ls)[LP], const double (*Rs)[LP], int K, doublex4 acc[2][2]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  for (int k = 0; k < K; k += 4) {
-    double av[2], bv[2];
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii) av[ii] = Ls[wr * 32 + ii * 16 + (lane & 15)][k + (lane >> 4)];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) bv[jj] = Rs[k + (lane >> 4)][wc * 32 + jj * 16 + (lane & 15)];
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        acc[ii][jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii], bv[jj], acc[ii][jj], 0, 0, 0);
-  }
-}
-
-// Visit the wave's accumulator elements: f(row, col, value) in tile coords.
-// v_mfma_f64_16x16x4f64 result layout: lane l, register r holds row
-// (l / 16) + 4 r, column l % 16 of the 16x16 block.
-template <typename F>
-__device__ __forceinline__ void tile_for_each(doublex4 acc[2][2], F f) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-#pragma unroll
-  for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        f(wr * 32 + ii * 16 + (lane >> 4) + 4 * r, wc * 32 + jj * 16 + (lane & 15), acc[ii][jj][r]);
 }
 
 // ------------------------------------------------------------ panel step
-// Blocks [0, nrow): L_ik for row block i = k1 + 64 b (in place in A).
-// Blocks [nrow, nrow + ncol): X[k, c0:c0+64] = X_kk R[k, c0:c0+64], c0 < k0
-// (in place in R).
+// Blocks [0, nrow): 32 rows i0 = k0 + kb + 32 b .. of block column k:
+//   L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T, stored column-major in LT
+//   (LT[(kl + m) * d + i] = L[i][k0 + m]).
+// Blocks [nrow, nrow + ncol): 32 columns c0 = 32 (b - nrow) < k0 of block
+// row k:  X_kc = X_kk (R_kc - L_kS' X_S'c), in place in R.
+// S' = [k0 - kl, k0) are the super-panel's earlier columns (kl <= 64).
+// Every operand load is issued before the first product.
+constexpr int PP = NB + 4;  // LDS pitch (doubles) of 64-wide panel tiles
+constexpr int PQ = 32 + 4;  // LDS pitch of 32-wide panel tiles
 __global__ void __launch_bounds__(256)
-hinv_panel(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, const double* __restrict__ Lbuf,
-           int nrow) {
-  __shared__ double Ls[NB][LP];
-  __shared__ double Rs[NB][LP];
-  const int tid = threadIdx.x;
-  const int k1 = k0 + kb;
+hinv_panel(const double* __restrict__ A, double* __restrict__ R, double* __restrict__ LT, int d, int k0, int kb,
+           int kl, const double* __restrict__ Xkk, const double* __restrict__ XkkT, int nrow) {
+  __shared__ double Lk[NB][PP];   // Lk[m][i] = L[k0 + i][s0 + m]
+  __shared__ double Xs[NB][PP];   // X_kk^T (row part) or X_kk (column part)
+  __shared__ double Lo[NB][PQ];   // row part: L[i0 + i][s0 + m] as Lo[m][i]; column part: X_S'c as Lo[m][c]
+  __shared__ double Cs[NB][PP];   // row part: C[i][m] (32 x 64); column part: C[i][c] (64 x 32)
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int s0 = k0 - kl;
   const int Kp = (kb + 3) & ~3;
-  doublex4 acc[2][2];
+  const bool rowpart = int(blockIdx.x) < nrow;
+  const int i0 = k0 + kb + 32 * blockIdx.x;           // row part
+  const int c0 = 32 * (int(blockIdx.x) - nrow);       // column part
+  double lk[16], x[16], lo[8], cv[8];
 #pragma unroll
-  for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
-  if (int(blockIdx.x) < nrow) {
-    const int r0 = k1 + NB * blockIdx.x;
-    // left: A[r0+i][k0+m]; right[m][j] = X_kk[j][m]
-    double v[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int e = tid + 256 * t;
-      const int i = e / NB, m = e % NB;
-      const bool ok = r0 + i < d && m < kb;
-      v[t] = A[ok ? int64_t(r0 + i) * d + k0 + m : 0];
-      v[t] = ok ? v[t] : 0.0;
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int e = tid + 256 * t;
-      const int i = e / NB, m = e % NB;
-      Ls[i][m] = v[t];
-      Rs[m][i] = Lbuf[i * NB + m];
-    }
-    __syncthreads();
-    tile_mma(Ls, Rs, Kp, acc);
-    tile_for_each(acc, [&](int i, int j, double v) {
-      if (r0 + i < d && j < kb) A[int64_t(r0 + i) * d + k0 + j] = v;
-    });
-  } else {
-    const int c0 = NB * (blockIdx.x - nrow);
-    // left: X_kk[i][m]; right[m][c] = R[k0+m][c0+c]
-    double v[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int e = tid + 256 * t;
-      const int i = e / NB, c = e % NB;
-      const bool ok = i < kb && c0 + c < k0;
-      v[t] = R[ok ? int64_t(k0 + i) * d + c0 + c : 0];
-      v[t] = ok ? v[t] : 0.0;
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int e = tid + 256 * t;
-      const int i = e / NB, c = e % NB;
-      Ls[i][c] = Lbuf[i * NB + c];
-      Rs[i][c] = v[t];
-    }
-    __syncthreads();
-    tile_mma(Ls, Rs, Kp, acc);
-    tile_for_each(acc, [&](int i, int c, double v) {
-      if (i < kb && c0 + c < k0) R[int64_t(k0 + i) * d + c0 + c] = v;
-    });
-  }
-}
-
-// ----------------------------------------------------------- update step
-// UT x UT output tiles (UT = 128 while the trailing matrix is large, 64 near
-// the end where a few big tiles would only add latency), K = kb <= 64. Each
-// of the 4 waves owns a (UT/2) x (UT/2) quarter of MFMA 16x16 blocks.
-// Operands are staged with every load issued before the first LDS store.
-constexpr int UP = 66;   // pitch (doubles) of the [UT][K] left operand
-
-// Stages a UT-row x 64-col fp64 block of M (rows r0.., cols k0..) into LDS,
-// Ls[r][k] (transpose = false) or Ls[k][r] (transpose = true). Elements with
-// row >= rmax or col >= k0 + kmax read as zero; all loads use clamped
-// in-bounds addresses and are issued before anything is stored.
-template <int UT, bool TRANSPOSE, typename Dst>
-__device__ __forceinline__ void stage_block(Dst Ls, const double* __restrict__ M, int d, int r0, int rmax, int k0,
-                                            int kmax) {
-  constexpr int PER = UT * 64 / 256;
-  const int tid = threadIdx.x;
-  double v[PER];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int e = tid + 256 * t;
-    const int r = e >> 6, k = e & 63;
-    const bool ok = (r0 + r < rmax) && (k < kmax);
-    v[t] = M[ok ? int64_t(r0 + r) * d + k0 + k : 0];
-    v[t] = ok ? v[t] : 0.0;
+  for (int t = 0; t < 16; ++t) {
+    const int e = tid + 256 * t, m = e >> 6, c = e & 63;
+    lk[t] = LT[m < kl ? int64_t(m) * d + k0 + (c < kb ? c : kb - 1) : 0];
+    x[t] = rowpart ? XkkT[e] : Xkk[e];
   }
 #pragma unroll
-  for (int t = 0; t < PER; ++t) {
+  for (int t = 0; t < 8; ++t) {
     const int e = tid + 256 * t;
-    const int r = e >> 6, k = e & 63;
-    if (TRANSPOSE)
-      Ls[k][r] = v[t];
+    if (rowpart) {
+      const int m = e >> 5, i = e & 31;
+      const int gi = i0 + i < d ? i0 + i : d - 1;
+      lo[t] = LT[m < kl ? int64_t(m) * d + gi : 0];
+      const int ii = e >> 6, mm = e & 63;  // C source: A[i0 + ii][k0 + mm]
+      const bool ok = i0 + ii < d && mm < kb;
+      cv[t] = A[ok ? int64_t(i0 + ii) * d + k0 + mm : 0];
+      cv[t] = ok ? cv[t] : 0.0;
+    } else {
+      const int m = e >> 5, c = e & 31;
+      lo[t] = R[m < kl ? int64_t(s0 + m) * d + c0 + c : 0];
+      const int ii = e >> 5, cc = e & 31;  // C source: R[k0 + ii][c0 + cc]
+      const bool ok = ii < kb;
+      cv[t] = R[ok ? int64_t(k0 + ii) * d + c0 + cc : 0];
+      cv[t] = ok ? cv[t] : 0.0;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int e = tid + 256 * t;
+    Lk[e >> 6][e & 63] = lk[t];
+    Xs[e >> 6][e & 63] = x[t];
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int e = tid + 256 * t;
+    Lo[e >> 5][e & 31] = lo[t];
+    if (rowpart)
+      Cs[e >> 6][e & 63] = cv[t];
     else
-      Ls[r][k] = v[t];
+      Cs[e >> 5][e & 31] = cv[t];
+  }
+  __syncthreads();
+  if (rowpart) {
+    // output 32 x 64: wave w owns rows 0..31 of column block w
+    const int ri[2] = {0, 16};
+    const int cj[2] = {16 * wave, 16 * wave};
+    doublex4 acc[2];
+    if (kl > 0) {
+      zero(acc);
+      blocks_mma<2, true>(acc, &Lo[0][0], PQ, &Lk[0][0], PP, ri, cj, kl);
+      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i][j] -= s; });
+      __syncthreads();
+    }
+    zero(acc);
+    blocks_mma<2, false>(acc, &Cs[0][0], PP, &Xs[0][0], PP, ri, cj, Kp);
+    // transpose through LDS (Lo is free again), then coalesced stores
+    __syncthreads();
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lk[j][i] = s; });
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int e = tid + 256 * t, m = e >> 5, i = e & 31;
+      if (m < kb && i0 + i < d) LT[int64_t(kl + m) * d + i0 + i] = Lk[m][i];
+    }
+  } else {
+    // output 64 x 32: wave w owns row block w, both column blocks
+    const int ri[2] = {16 * wave, 16 * wave};
+    const int cj[2] = {0, 16};
+    doublex4 acc[2];
+    if (kl > 0) {
+      zero(acc);
+      blocks_mma<2, true>(acc, &Lk[0][0], PP, &Lo[0][0], PQ, ri, cj, kl);
+      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i][j] -= s; });
+      __syncthreads();
+    }
+    zero(acc);
+    // X_kc = X_kk C: A operand X_kk[i][m] row-major in Xs, B operand C[m][c]
+    blocks_mma<2, false>(acc, &Xs[0][0], PP, &Cs[0][0], PP, ri, cj, Kp);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
+      if (i < kb) R[int64_t(k0 + i) * d + c0 + j] = s;
+    });
   }
 }
 
-template <int UT, int RQ>
-__device__ __forceinline__ void tileU_mma(const double (*Ls)[UP], const double (*Rs)[RQ], int K,
-                                          doublex4 acc[UT / 32][UT / 32]) {
-  constexpr int BL = UT / 32;
+// ---------------------------------------------------------- trailing step
+// After the super-panel [s0, s1) (K = s1 - s0, a multiple of 8):
+//   blocks [0, nA):           lower 128-tiles (ti >= tj) at s1:
+//                             A_ij -= L_iS L_jS^T
+//   blocks [nA, nA + nT nC):  R tile rows s1 + 128 ti, columns 128 tc < s1:
+//                             R_ic -= L_iS X_Sc
+// Each wave owns a 64x64 quarter (4x4 MFMA blocks, 16 independent chains)
+// and loads its operands straight from memory (L_S column-major in LT,
+// X_S as rows s0.. of R), one k-step ahead. The accumulators start from the
+// old tile, so the tile is read once and written once.
+__global__ void __launch_bounds__(256, 2)
+hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, int s0, int s1,
+           int nT) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  for (int k = 0; k < K; k += 4) {
-    double av[BL], bv[BL];
-#pragma unroll
-    for (int ii = 0; ii < BL; ++ii) av[ii] = Ls[wr * (UT / 2) + ii * 16 + (lane & 15)][k + (lane >> 4)];
-#pragma unroll
-    for (int jj = 0; jj < BL; ++jj) bv[jj] = Rs[k + (lane >> 4)][wc * (UT / 2) + jj * 16 + (lane & 15)];
-#pragma unroll
-    for (int ii = 0; ii < BL; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < BL; ++jj)
-        acc[ii][jj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ii], bv[jj], acc[ii][jj], 0, 0, 0);
-  }
-}
-
-// M[tile element] -= acc for the elements `keep` selects. All loads are
-// issued unconditionally (masked-off ones read M[0]) before any store, so
-// the tile costs one memory round trip; only the stores are masked.
-// v_mfma_f64_16x16x4f64 layout: lane l, register r -> row l/16 + 4r, col l%16.
-template <int UT, typename Keep>
-__device__ __forceinline__ void rmw_sub(double* __restrict__ M, int d, int r0, int c0,
-                                        doublex4 acc[UT / 32][UT / 32], Keep keep) {
-  constexpr int BL = UT / 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  double old[BL][BL][4];
-#pragma unroll
-  for (int ii = 0; ii < BL; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < BL; ++jj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gi = r0 + wr * (UT / 2) + ii * 16 + (lane >> 4) + 4 * r;
-        const int gj = c0 + wc * (UT / 2) + jj * 16 + (lane & 15);
-        old[ii][jj][r] = M[keep(gi, gj) ? int64_t(gi) * d + gj : 0];
-      }
-#pragma unroll
-  for (int ii = 0; ii < BL; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < BL; ++jj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int gi = r0 + wr * (UT / 2) + ii * 16 + (lane >> 4) + 4 * r;
-        const int gj = c0 + wc * (UT / 2) + jj * 16 + (lane & 15);
-        if (keep(gi, gj)) M[int64_t(gi) * d + gj] = old[ii][jj][r] - acc[ii][jj][r];
-      }
-}
-
-// Blocks [0, nA): lower UT-tiles (ti >= tj) of the trailing matrix at k1:
-//   A_ij -= L_i L_j^T.
-// Blocks [nA, nA + nT * nC): R[k1 + UT ti, UT tc] -= L_i X[k, UT tc].
-template <int UT>
-__global__ void __launch_bounds__(256)
-hinv_update(double* __restrict__ A, double* __restrict__ R, int d, int k0, int kb, int nT, int nC) {
-  constexpr int RQ = UT + 4;
-  constexpr int BL = UT / 32;
-  __shared__ double Ls[UT][UP];
-  __shared__ double Rs[NB][RQ];
-  const int k1 = k0 + kb;
-  const int Kp = (kb + 3) & ~3;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int K = s1 - s0;
   const int nA = nT * (nT + 1) / 2;
   int b = blockIdx.x;
-  doublex4 acc[BL][BL];
-#pragma unroll
-  for (int ii = 0; ii < BL; ++ii)
-#pragma unroll
-    for (int jj = 0; jj < BL; ++jj) acc[ii][jj] = doublex4{0, 0, 0, 0};
-  if (b < nA) {
+  const bool apart = b < nA;
+  int r0, c0;
+  if (apart) {
     int ti = 0;
     while (b > ti) {
       b -= ti + 1;
       ++ti;
     }
-    const int tj = b;
-    const int r0 = k1 + UT * ti, c0 = k1 + UT * tj;
-    stage_block<UT, false>(Ls, A, d, r0, d, k0, kb);
-    stage_block<UT, true>(Rs, A, d, c0, d, k0, kb);  // Rs[m][j] = L[c0 + j][k0 + m]
-    __syncthreads();
-    tileU_mma<UT, RQ>(Ls, Rs, Kp, acc);
-    rmw_sub<UT>(A, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj <= gi; });
+    r0 = s1 + 128 * ti;
+    c0 = s1 + 128 * b;
   } else {
     b -= nA;
-    const int ti = b / nC, tc = b % nC;
-    const int r0 = k1 + UT * ti, c0 = UT * tc;
-    stage_block<UT, false>(Ls, A, d, r0, d, k0, kb);
-    {
-      // Rs[m][c] = X[k0 + m][c0 + c]; X is lower triangular inside the
-      // diagonal block (R's upper part is never written, so it is masked).
-      constexpr int PER = 64 * UT / 256;
-      const int tid = threadIdx.x;
-      double v[PER];
-#pragma unroll
-      for (int t = 0; t < PER; ++t) {
-        const int e = tid + 256 * t;  // 64 rows x UT cols
-        const int m = e / UT, c = e % UT;
-        const int g = c0 + c;
-        const bool ok = m < kb && g < k1 && g <= k0 + m;
-        v[t] = R[ok ? int64_t(k0 + m) * d + g : 0];
-        v[t] = ok ? v[t] : 0.0;
-      }
-#pragma unroll
-      for (int t = 0; t < PER; ++t) {
-        const int e = tid + 256 * t;
-        Rs[e / UT][e % UT] = v[t];
-      }
-    }
-    __syncthreads();
-    tileU_mma<UT, RQ>(Ls, Rs, Kp, acc);
-    rmw_sub<UT>(R, d, r0, c0, acc, [&](int gi, int gj) { return gi < d && gj < k1; });
+    r0 = s1 + 128 * (b % nT);
+    c0 = 128 * (b / nT);
   }
+  double* __restrict__ M = apart ? A : R;
+  const int rw = r0 + 64 * wr, cw = c0 + 64 * wc;
+  // old tile into the accumulators (clamped addresses; rows past d and the
+  // upper half of diagonal A tiles are computed but never stored)
+  doublex4 acc[4][4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int gi = rw + ii * 16 + lk + 4 * r, gj = cw + jj * 16 + lr;
+        gi = gi < d ? gi : d - 1;
+        gj = gj < d ? gj : d - 1;
+        acc[ii][jj][r] = M[int64_t(gi) * d + gj];
+      }
+  // operand addresses for k = lk: A op LT[k][row], B op LT[k][col] or R[s0 + k][col]
+  const double* pa[4];
+  const double* pb[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    int gi = rw + t * 16 + lr, gj = cw + t * 16 + lr;
+    gi = gi < d ? gi : d - 1;
+    gj = gj < d ? gj : d - 1;
+    pa[t] = LT + int64_t(lk) * d + gi;
+    pb[t] = apart ? LT + int64_t(lk) * d + gj : R + int64_t(s0 + lk) * d + gj;
+  }
+  const int64_t kstep = 4 * int64_t(d);
+  double a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    a0[t] = -pa[t][0];
+    b0[t] = pb[t][0];
+  }
+  for (int k = 0; k < K; k += 8) {
+    const int64_t o1 = int64_t(k + 4) * d;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      a1[t] = -pa[t][o1];
+      b1[t] = pb[t][o1];
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = mfma64(a0[ii], b0[jj], acc[ii][jj]);
+    const int64_t o2 = (k + 8 < K) ? o1 + kstep : o1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      a0[t] = -pa[t][o2];
+      b0[t] = pb[t][o2];
+    }
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = mfma64(a1[ii], b1[jj], acc[ii][jj]);
+  }
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gi = rw + ii * 16 + lk + 4 * r, gj = cw + jj * 16 + lr;
+        const bool keep = gi < d && (apart ? gj <= gi : gj < s1);
+        if (keep) M[int64_t(gi) * d + gj] = acc[ii][jj][r];
+      }
 }
 
 // U[i][j] = X[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -446,19 +521,23 @@ hinv_write_u(const double* __restrict__ R, int d, float* __restrict__ U) {
 }
 
 struct HinvWs {
-  double *A, *R, *lam, *Lbuf;
+  double *A, *R, *LT, *lam, *Xkk, *XkkT;
   size_t bytes;
 };
 
 HinvWs carve(void* ws, int64_t d) {
   HinvWs w{};
   const size_t mat = align_up(size_t(d) * d * sizeof(double), 256);
+  const size_t panel = align_up(size_t(KS) * d * sizeof(double), 256);
+  const size_t blk = align_up(NB * NB * sizeof(double), 256);
   char* p = static_cast<char*>(ws);
   w.A = reinterpret_cast<double*>(p);
   w.R = reinterpret_cast<double*>(p + mat);
-  w.lam = reinterpret_cast<double*>(p + 2 * mat);
-  w.Lbuf = reinterpret_cast<double*>(p + 2 * mat + 256);
-  w.bytes = 2 * mat + 256 + align_up(NB * NB * sizeof(double), 256);
+  w.LT = reinterpret_cast<double*>(p + 2 * mat);
+  w.lam = reinterpret_cast<double*>(p + 2 * mat + panel);
+  w.Xkk = reinterpret_cast<double*>(p + 2 * mat + panel + 256);
+  w.XkkT = reinterpret_cast<double*>(p + 2 * mat + panel + 256 + blk);
+  w.bytes = 2 * mat + panel + 256 + 2 * blk;
   return w;
 }
 
@@ -482,29 +561,27 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
   const int di = int(d);
   hipLaunchKernelGGL(hinv_lambda, dim3(1), dim3(256), 0, s, H, di, damp, w.lam, lambda_out, info);
   const int nb32 = (di + 31) / 32;
-  hipLaunchKernelGGL(hinv_setup, dim3(unsigned(nb32 * (nb32 + 1) / 2)), dim3(256), 0, s, H, di, w.lam, w.A, w.R);
+  hipLaunchKernelGGL(hinv_setup, dim3(unsigned(nb32 * (nb32 + 1) / 2)), dim3(256), 0, s, H, di, w.lam, w.A);
+  const int64_t eye_blocks = (int64_t(di) * di + 511) / 512;
+  hipLaunchKernelGGL(hinv_eye, dim3(unsigned(eye_blocks < 4096 ? eye_blocks : 4096)), dim3(256), 0, s, w.R, di);
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
-  for (int k0 = 0; k0 < di; k0 += NB) {
-    const int kb = di - k0 < NB ? di - k0 : NB;
-    const int k1 = k0 + kb;
-    hipLaunchKernelGGL(hinv_diag, dim3(1), dim3(256), 0, s, w.A, w.R, di, k0, kb, w.Lbuf, info);
-    const int nrow = (di - k1 + NB - 1) / NB;
-    const int ncol = (k0 + NB - 1) / NB;
-    if (nrow + ncol > 0)
-      hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, di, k0, kb, w.Lbuf,
-                         nrow);
-    // 128-wide update tiles while they fill the GPU, 64-wide near the end.
-    const int rem = di - k1;
-    const int n128 = (rem + 127) / 128;
-    if (n128 * (n128 + 1) / 2 >= 256) {
-      const int nT = n128, nC = (k1 + 127) / 128;
-      const int nblk = nT * (nT + 1) / 2 + nT * nC;
-      hipLaunchKernelGGL(hinv_update<128>, dim3(unsigned(nblk)), dim3(256), 0, s, w.A, w.R, di, k0, kb, nT, nC);
-    } else {
-      const int nT = (rem + 63) / 64, nC = (k1 + 63) / 64;
-      const int nblk = nT * (nT + 1) / 2 + nT * nC;
-      if (nblk > 0)
-        hipLaunchKernelGGL(hinv_update<64>, dim3(unsigned(nblk)), dim3(256), 0, s, w.A, w.R, di, k0, kb, nT, nC);
+  for (int s0 = 0; s0 < di; s0 += KS) {
+    const int s1 = di - s0 < KS ? di : s0 + KS;
+    for (int k0 = s0; k0 < s1; k0 += NB) {
+      const int kb = s1 - k0 < NB ? s1 - k0 : NB;
+      const int kl = k0 - s0;
+      hipLaunchKernelGGL(hinv_diag, dim3(1), dim3(256), 0, s, w.A, w.R, w.LT, di, k0, kb, kl, w.Xkk, w.XkkT, info);
+      const int nrow = (di - k0 - kb + 31) / 32;
+      const int ncol = k0 / 32;
+      if (nrow + ncol > 0)
+        hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, w.LT, di, k0, kb, kl,
+                           w.Xkk, w.XkkT, nrow);
+    }
+    if (s1 < di) {
+      const int nT = (di - s1 + 127) / 128;
+      const int nC = s1 / 128;
+      hipLaunchKernelGGL(hinv_trail, dim3(unsigned(nT * (nT + 1) / 2 + nT * nC)), dim3(256), 0, s, w.A, w.R, w.LT,
+                         di, s0, s1, nT);
     }
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }
