@@ -28,8 +28,7 @@
 // its diag and panel steps have run. All products use the fp64 MFMA
 // (v_mfma_f64_16x16x4f64). The trailing update, which holds almost all of
 // the flops, reads the trailing matrix once per 128 columns instead of once
-// per 64, and reads its operands straight from L2 with 16 independent MFMA
-// chains per wave.
+// per 64 and keeps 16 independent MFMA chains per wave.
 #include <utility>
 
 #include "gptq_common.h"
@@ -409,19 +408,30 @@ hinv_panel(const double* __restrict__ A, double* __restrict__ R, double* __restr
 }
 
 // ---------------------------------------------------------- trailing step
-// After the super-panel [s0, s1) (K = s1 - s0, a multiple of 8):
-//   blocks [0, nA):           lower 128-tiles (ti >= tj) at s1:
+// After the super-panel [s0, s1) (K = s1 - s0 = KS), with T x T tiles:
+//   blocks [0, nA):           lower tiles (ti >= tj) at s1:
 //                             A_ij -= L_iS L_jS^T
-//   blocks [nA, nA + nT nC):  R tile rows s1 + 128 ti, columns 128 tc < s1:
+//   blocks [nA, nA + nT nC):  R tile rows s1 + T ti, columns T tc < s1:
 //                             R_ic -= L_iS X_Sc
-// Each wave owns a 64x64 quarter (4x4 MFMA blocks, 16 independent chains)
-// and loads its operands straight from memory (L_S column-major in LT,
-// X_S as rows s0.. of R), one k-step ahead. The accumulators start from the
-// old tile, so the tile is read once and written once.
+// Each wave owns a (T/2) x (T/2) quarter (T = 128: 16 independent MFMA
+// chains; T = 64, used when big tiles would leave CUs idle: 4 chains). The
+// operands (L_S column-major in LT; X_S as rows s0.. of R) pass through LDS
+// in chunks of 16 k; the next chunk's loads are in flight while the current
+// one is multiplied. The accumulators start from the old tile, so it is read
+// once and written once.
+constexpr int TK = 16;  // k per LDS chunk
+template <int T>
 __global__ void __launch_bounds__(256, 2)
 hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, int s0, int s1,
            int nT) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int TPITCH = T + 4;
+  constexpr int BL = T / 32;           // 16x16 blocks per wave dimension
+  constexpr int STEP = 256 / T;        // k rows loaded per pass
+  constexpr int U = TK / STEP;         // loads per thread per chunk and operand
+  __shared__ double As[TK][TPITCH];    // As[k][i] = -L[r0 + i][s0 + k]
+  __shared__ double Bs[TK][TPITCH];    // Bs[k][j] = L[c0 + j][s0 + k] or X[s0 + k][c0 + j]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int lr = lane & 15, lk = lane >> 4;
   const int K = s1 - s0;
@@ -435,22 +445,35 @@ hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restr
       b -= ti + 1;
       ++ti;
     }
-    r0 = s1 + 128 * ti;
-    c0 = s1 + 128 * b;
+    r0 = s1 + T * ti;
+    c0 = s1 + T * b;
   } else {
     b -= nA;
-    r0 = s1 + 128 * (b % nT);
-    c0 = 128 * (b / nT);
+    r0 = s1 + T * (b % nT);
+    c0 = T * (b / nT);
   }
   double* __restrict__ M = apart ? A : R;
-  const int rw = r0 + 64 * wr, cw = c0 + 64 * wc;
+  // chunk loads: thread t covers column t % T of k rows t / T + STEP u
+  const int li = tid % T, lk0 = tid / T;
+  const int ga = r0 + li < d ? r0 + li : d - 1;
+  const int gb = c0 + li < d ? c0 + li : d - 1;
+  const double* __restrict__ srcA = LT + ga;
+  const double* __restrict__ srcB = apart ? LT + gb : R + int64_t(s0) * d + gb;
+  double la[U], lb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t o = int64_t(lk0 + STEP * u) * d;
+    la[u] = srcA[o];
+    lb[u] = srcB[o];
+  }
   // old tile into the accumulators (clamped addresses; rows past d and the
   // upper half of diagonal A tiles are computed but never stored)
-  doublex4 acc[4][4];
+  const int rw = r0 + (T / 2) * wr, cw = c0 + (T / 2) * wc;
+  doublex4 acc[BL][BL];
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+  for (int ii = 0; ii < BL; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < BL; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         int gi = rw + ii * 16 + lk + 4 * r, gj = cw + jj * 16 + lr;
@@ -458,50 +481,40 @@ hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restr
         gj = gj < d ? gj : d - 1;
         acc[ii][jj][r] = M[int64_t(gi) * d + gj];
       }
-  // operand addresses for k = lk: A op LT[k][row], B op LT[k][col] or R[s0 + k][col]
-  const double* pa[4];
-  const double* pb[4];
+  for (int kc = 0; kc < K; kc += TK) {
+    __syncthreads();  // the previous chunk's products are done
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    int gi = rw + t * 16 + lr, gj = cw + t * 16 + lr;
-    gi = gi < d ? gi : d - 1;
-    gj = gj < d ? gj : d - 1;
-    pa[t] = LT + int64_t(lk) * d + gi;
-    pb[t] = apart ? LT + int64_t(lk) * d + gj : R + int64_t(s0 + lk) * d + gj;
-  }
-  const int64_t kstep = 4 * int64_t(d);
-  double a0[4], b0[4], a1[4], b1[4];
+    for (int u = 0; u < U; ++u) {
+      As[lk0 + STEP * u][li] = -la[u];
+      Bs[lk0 + STEP * u][li] = lb[u];
+    }
+    __syncthreads();
+    if (kc + TK < K) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    a0[t] = -pa[t][0];
-    b0[t] = pb[t][0];
-  }
-  for (int k = 0; k < K; k += 8) {
-    const int64_t o1 = int64_t(k + 4) * d;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      a1[t] = -pa[t][o1];
-      b1[t] = pb[t][o1];
+      for (int u = 0; u < U; ++u) {
+        const int64_t o = int64_t(kc + TK + lk0 + STEP * u) * d;
+        la[u] = srcA[o];
+        lb[u] = srcB[o];
+      }
     }
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
+    for (int k = 0; k < TK; k += 4) {
+      double a[BL], bb[BL];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = mfma64(a0[ii], b0[jj], acc[ii][jj]);
-    const int64_t o2 = (k + 8 < K) ? o1 + kstep : o1;
+      for (int t = 0; t < BL; ++t) {
+        a[t] = As[k + lk][(T / 2) * wr + 16 * t + lr];
+        bb[t] = Bs[k + lk][(T / 2) * wc + 16 * t + lr];
+      }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      a0[t] = -pa[t][o2];
-      b0[t] = pb[t][o2];
+      for (int ii = 0; ii < BL; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < BL; ++jj) acc[ii][jj] = mfma64(a[ii], bb[jj], acc[ii][jj]);
     }
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acc[ii][jj] = mfma64(a1[ii], b1[jj], acc[ii][jj]);
   }
 #pragma unroll
-  for (int ii = 0; ii < 4; ++ii)
+  for (int ii = 0; ii < BL; ++ii)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < BL; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int gi = rw + ii * 16 + lk + 4 * r, gj = cw + jj * 16 + lr;
@@ -578,10 +591,16 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
                            w.Xkk, w.XkkT, nrow);
     }
     if (s1 < di) {
-      const int nT = (di - s1 + 127) / 128;
-      const int nC = s1 / 128;
-      hipLaunchKernelGGL(hinv_trail, dim3(unsigned(nT * (nT + 1) / 2 + nT * nC)), dim3(256), 0, s, w.A, w.R, w.LT,
-                         di, s0, s1, nT);
+      // 128-tiles while there are at least four per CU, 64-tiles below that
+      const int nT = (di - s1 + 127) / 128, nC = s1 / 128;
+      const int64_t n128 = int64_t(nT) * (nT + 1) / 2 + int64_t(nT) * nC;
+      if (n128 >= 4 * 256) {
+        hipLaunchKernelGGL(hinv_trail<128>, dim3(unsigned(n128)), dim3(256), 0, s, w.A, w.R, w.LT, di, s0, s1, nT);
+      } else {
+        const int mT = (di - s1 + 63) / 64, mC = s1 / 64;
+        const int64_t n64 = int64_t(mT) * (mT + 1) / 2 + int64_t(mT) * mC;
+        hipLaunchKernelGGL(hinv_trail<64>, dim3(unsigned(n64)), dim3(256), 0, s, w.A, w.R, w.LT, di, s0, s1, mT);
+      }
     }
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }

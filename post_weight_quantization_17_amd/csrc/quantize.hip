@@ -12,7 +12,8 @@
 // Design (gfx950): rows are independent given U, so one persistent
 // workgroup owns 16 rows for the whole sweep and needs no grid-wide
 // synchronization. Per 128-column block it
-//   1. stages U[blk, blk] (64 KB fp32) and 1/U_qq in LDS;
+//   1. stages U[blk, blk] (64 KB fp32) in LDS and 1/U_qq of each lane's
+//      columns in registers;
 //   2. runs the 128 sequential column steps with each row spread over one
 //      16-lane DPP row (8 columns per lane, interleaved): the current value
 //      of column q is broadcast from its owner lane with DPP row_newbcast,
@@ -84,14 +85,77 @@ __device__ __forceinline__ float div_rn(float x, float s, float rs) {
   return fmaf(r, rs, q);
 }
 
+// Whole-tile form of the deferred update W[rows, i2:] -= E U[i1:i2, i2:]
+// (i2 = i1 + QB), used when the layer needs no bounds test anywhere:
+// d_col % 64 == 0, d_row % 16 == 0, W and U 16-byte aligned. Same MFMA
+// mapping as the checked form in the kernel below (the workgroup's 16 rows
+// are one v_mfma_f32_16x16x4f32 M tile, Es the A operand, U rows i1.. the B
+// operand; wave w takes the 64-column chunks i2 + 64 w + 256 c). With no
+// branches in the loop, the next chunk's W tile (the accumulators' start
+// value) and the U rows RING k-steps ahead, across chunk boundaries, stay in
+// flight while the current chunk's MFMAs run.
 template <typename WT>
+__device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, float* __restrict__ Wf,
+                                                      const float* __restrict__ U, const float (*Es)[QB + 4],
+                                                      int d_col, int row0, int i1, bool first) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lk = lane >> 4;
+  const int nb0 = i1 + QB + 64 * wave;
+  const int nch = nb0 < d_col ? (d_col - nb0 + 255) / 256 : 0;
+  const size_t ustep = size_t(4) * d_col;
+  const float* __restrict__ ub = U + size_t(i1 + lk) * d_col + nb0 + 4 * li;
+  const size_t wrow = size_t(row0 + 4 * lk) * d_col + nb0 + 4 * li;
+  auto ldb = [&](int ch, int t) -> floatx4 { return load4(ub + 256 * ch + t * ustep); };
+  auto ldw = [&](int ch, floatx4 (&v)[4]) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const size_t off = wrow + size_t(r) * d_col + 256 * ch;
+      v[r] = first ? load4(W + off) : load4(Wf + off);
+    }
+  };
+  constexpr int RING = 8;
+  constexpr int KS4 = QB / 4;  // k-steps per chunk
+  floatx4 ring[RING];
+  floatx4 wn[4];
+  if (nch > 0) {
+#pragma unroll
+    for (int t = 0; t < RING; ++t) ring[t] = ldb(0, t);
+    ldw(0, wn);
+  }
+  for (int ch = 0; ch < nch; ++ch) {
+    floatx4 acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t][r] = wn[r][t];
+    const bool more = ch + 1 < nch;
+    if (more) ldw(ch + 1, wn);
+#pragma unroll
+    for (int t = 0; t < KS4; ++t) {
+      const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
+      const floatx4 b = ring[t % RING];
+      if (t + RING < KS4)
+        ring[t % RING] = ldb(ch, t + RING);
+      else if (more)
+        ring[t % RING] = ldb(ch + 1, t + RING - KS4);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[v], 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const size_t off = wrow + size_t(r) * d_col + 256 * ch;
+      *reinterpret_cast<float4*>(Wf + off) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+    }
+  }
+}
+
+template <typename WT, bool WHOLE>
 __global__ void __launch_bounds__(QT, 2)
 gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __restrict__ U, int d_row, int d_col,
            int bits, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
            int32_t* __restrict__ zeros, uint32_t* __restrict__ packed, int nwords, float* __restrict__ row_loss,
            double* __restrict__ wg_loss) {
   __shared__ __attribute__((aligned(16))) float Ud[QB][QB];
-  __shared__ float dinv[QB];
   __shared__ float Es[QR][QB + 4];
   __shared__ uint8_t Cs[QR][QB];
   __shared__ double Lsum[QR];
@@ -169,15 +233,16 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       wr[m] = v;
     }
     __syncthreads();
-    if (tid < QB) dinv[tid] = 1.f / Ud[tid][tid];
-    __syncthreads();
+    // 1/U_qq of the lane's own columns; step q broadcasts it from q's owner.
+    float dv[QM];
+#pragma unroll
+    for (int m = 0; m < QM; ++m) dv[m] = 1.f / Ud[16 * m + sub][16 * m + sub];
 
-    // 2. The 128 sequential column steps. Row q+1 of the U block and
-    //    1/U_{q+1,q+1} are loaded while step q runs; the empty asm with a
-    //    memory clobber keeps the steps in program order (no store merging
-    //    or load hoisting across steps, which would lengthen live ranges).
+    // 2. The 128 sequential column steps. Row q+1 of the U block is loaded
+    //    while step q runs; the empty asm with a memory clobber keeps the
+    //    steps in program order (no store merging or load hoisting across
+    //    steps, which would lengthen live ranges).
     float uc[QM], un[QM];
-    float dc = dinv[0], dn = 0.f;
 #pragma unroll
     for (int mm = 0; mm < QM; ++mm) uc[mm] = Ud[0][16 * mm + sub];
     static_for<0, QB>([&](auto qc) {
@@ -187,8 +252,8 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       if constexpr (q + 1 < QB) {
 #pragma unroll
         for (int mm = (q + 1) / 16; mm < QM; ++mm) un[mm] = Ud[q + 1][16 * mm + sub];
-        dn = dinv[q + 1];
       }
+      const float dc = row_bcast<o>(dv[m]);
       if constexpr (o == 0) {
         if (group > 0 && q < nvalid && (i1 + q) % group == 0) {
           float mn = 0.f, mx = 0.f;
@@ -226,6 +291,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
 #pragma unroll
       for (int mm = m; mm < QM; ++mm) wr[mm] = fmaf(-e, uc[mm], wr[mm]);
       lacc = fma(0.5 * double(e), double(e), lacc);
+      asm volatile("" : "+v"(lacc));  // accumulate now, not deferred across steps
       // Every lane of the row holds the same code and error: all 16 store
       // the same value to the row's LDS slot, so no owner test is needed.
       Cs[rloc][q] = uint8_t(c);
@@ -233,7 +299,6 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       if constexpr (q + 1 < QB) {
 #pragma unroll
         for (int mm = (q + 1) / 16; mm < QM; ++mm) uc[mm] = un[mm];
-        dc = dn;
       }
       asm volatile("" ::: "memory");
     });
@@ -255,7 +320,8 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
 
     // 4. Deferred update of the later columns: W[:, i2:] -= E U[blk, i2:].
     const int i2 = i1 + QB;
-    if (i2 < d_col) {
+    if (WHOLE && i2 < d_col) trailing_update_whole(W, Wf, U, Es, d_col, row0, i1, first);
+    if (!WHOLE && i2 < d_col) {
       const int li = lane & 15, lk = lane >> 4;
       for (int n0 = i2 + 64 * wave; n0 < d_col; n0 += 256) {
         const int col = n0 + 4 * li;
@@ -418,14 +484,20 @@ extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int
   const int esz = wdtype == GPTQ_F16 ? 2 : 4;
   const int vec4 = (d_col % 4 == 0) && (reinterpret_cast<uintptr_t>(W) % (4 * esz) == 0) &&
                    (reinterpret_cast<uintptr_t>(U) % 16 == 0) ? 1 : 0;
-  if (wdtype == GPTQ_F16)
-    hipLaunchKernelGGL(gptq_sweep<__half>, dim3(nwg), dim3(QT), 0, s, static_cast<const __half*>(W), w.Wf, U,
-                       int(d_row), int(d_col), bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed,
-                       nwords, row_loss, w.wg_loss);
-  else
-    hipLaunchKernelGGL(gptq_sweep<float>, dim3(nwg), dim3(QT), 0, s, static_cast<const float*>(W), w.Wf, U,
-                       int(d_row), int(d_col), bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed,
-                       nwords, row_loss, w.wg_loss);
+  // Whole-tile layers (every chunk of the deferred update complete, every
+  // workgroup's 16 rows present) take the branch-free update.
+  const bool whole = vec4 && d_col % 64 == 0 && d_row % QR == 0;
+  if (wdtype == GPTQ_F16) {
+    auto k = whole ? gptq_sweep<__half, true> : gptq_sweep<__half, false>;
+    hipLaunchKernelGGL(k, dim3(nwg), dim3(QT), 0, s, static_cast<const __half*>(W), w.Wf, U, int(d_row), int(d_col),
+                       bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
+                       w.wg_loss);
+  } else {
+    auto k = whole ? gptq_sweep<float, true> : gptq_sweep<float, false>;
+    hipLaunchKernelGGL(k, dim3(nwg), dim3(QT), 0, s, static_cast<const float*>(W), w.Wf, U, int(d_row), int(d_col),
+                       bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
+                       w.wg_loss);
+  }
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   hipLaunchKernelGGL(loss_final, dim3(1), dim3(256), 0, s, w.wg_loss, int(nwg), loss);
   return launch_status();
