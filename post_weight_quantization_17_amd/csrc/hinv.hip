@@ -29,6 +29,7 @@
 // (v_mfma_f64_16x16x4f64). The trailing update, which holds almost all of
 // the flops, reads the trailing matrix once per 128 columns instead of once
 // per 64 and keeps 16 independent MFMA chains per wave.
+#include <mutex>
 #include <utility>
 
 #include "gptq_common.h"
@@ -408,11 +409,12 @@ hinv_panel(const double* __restrict__ A, double* __restrict__ R, double* __restr
 }
 
 // ---------------------------------------------------------- trailing step
-// After the super-panel [s0, s1) (K = s1 - s0 = KS), with T x T tiles:
-//   blocks [0, nA):           lower tiles (ti >= tj) at s1:
-//                             A_ij -= L_iS L_jS^T
-//   blocks [nA, nA + nT nC):  R tile rows s1 + T ti, columns T tc < s1:
-//                             R_ic -= L_iS X_Sc
+// After the super-panel S = [s0, s1) (K = s1 - s0 = KS), with T x T tiles:
+//   blocks [0, nA):   A tiles (lower part only):  A_ij -= L_iS L_jS^T
+//                     either the lower triangle of tiles from (ra0, ra0), or
+//                     a rectangle from (ra0, ca0)
+//   blocks [nA, ..):  R tiles, rows from rr0, columns T tc < s1:
+//                     R_ic -= L_iS X_Sc
 // Each wave owns a (T/2) x (T/2) quarter (T = 128: 16 independent MFMA
 // chains; T = 64, used when big tiles would leave CUs idle: 4 chains). The
 // operands (L_S column-major in LT; X_S as rows s0.. of R) pass through LDS
@@ -420,10 +422,15 @@ hinv_panel(const double* __restrict__ A, double* __restrict__ R, double* __restr
 // one is multiplied. The accumulators start from the old tile, so it is read
 // once and written once.
 constexpr int TK = 16;  // k per LDS chunk
+struct TrailSpec {
+  int s0, s1;     // the super-panel whose columns are applied (K = s1 - s0)
+  int ra0, naR;   // A part: first row (and, if tri, first column), tile rows
+  int ca0, naC;   // A part: first column and tile columns of a rectangle; naC = 0: lower triangle
+  int rr0, nrR;   // R part: first row, tile rows (columns: tiles 0 .. s1 / T)
+};
 template <int T>
 __global__ void __launch_bounds__(256, 2)
-hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, int s0, int s1,
-           int nT) {
+hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, TrailSpec sp) {
   constexpr int TPITCH = T + 4;
   constexpr int BL = T / 32;           // 16x16 blocks per wave dimension
   constexpr int STEP = 256 / T;        // k rows loaded per pass
@@ -434,23 +441,31 @@ hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restr
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int lr = lane & 15, lk = lane >> 4;
+  const int s0 = sp.s0, s1 = sp.s1;
   const int K = s1 - s0;
-  const int nA = nT * (nT + 1) / 2;
+  const bool tri = sp.naC == 0;
+  const int nA = tri ? sp.naR * (sp.naR + 1) / 2 : sp.naR * sp.naC;
   int b = blockIdx.x;
   const bool apart = b < nA;
   int r0, c0;
   if (apart) {
-    int ti = 0;
-    while (b > ti) {
-      b -= ti + 1;
-      ++ti;
+    if (tri) {
+      int ti = 0;
+      while (b > ti) {
+        b -= ti + 1;
+        ++ti;
+      }
+      r0 = sp.ra0 + T * ti;
+      c0 = sp.ra0 + T * b;
+    } else {
+      r0 = sp.ra0 + T * (b / sp.naC);
+      c0 = sp.ca0 + T * (b % sp.naC);
+      if (c0 > r0 + T - 1) return;  // entirely above the diagonal (whole workgroup)
     }
-    r0 = s1 + T * ti;
-    c0 = s1 + T * b;
   } else {
     b -= nA;
-    r0 = s1 + T * (b % nT);
-    c0 = T * (b / nT);
+    r0 = sp.rr0 + T * (b % sp.nrR);
+    c0 = T * (b / sp.nrR);
   }
   double* __restrict__ M = apart ? A : R;
   // chunk loads: thread t covers column t % T of k rows t / T + STEP u
@@ -541,7 +556,7 @@ struct HinvWs {
 HinvWs carve(void* ws, int64_t d) {
   HinvWs w{};
   const size_t mat = align_up(size_t(d) * d * sizeof(double), 256);
-  const size_t panel = align_up(size_t(KS) * d * sizeof(double), 256);
+  const size_t panel = align_up(size_t(2) * KS * d * sizeof(double), 256);  // double buffered
   const size_t blk = align_up(NB * NB * sizeof(double), 256);
   char* p = static_cast<char*>(ws);
   w.A = reinterpret_cast<double*>(p);
@@ -554,6 +569,51 @@ HinvWs carve(void* ws, int64_t d) {
   return w;
 }
 
+// Per-device auxiliary stream and events for the look-ahead (created once,
+// kept until the process ends). Enqueueing a factorization holds a lock, so
+// concurrent callers cannot interleave their event records.
+struct AuxCtx {
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, chain[2] = {}, trail[2] = {};
+  bool ready = false;
+};
+std::mutex g_aux_mu;
+AuxCtx g_aux[64];
+
+AuxCtx* aux_context() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  AuxCtx& c = g_aux[dev];
+  if (!c.ready) {
+    if (hipStreamCreateWithFlags(&c.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    hipEvent_t* evs[6] = {&c.fork, &c.join, &c.chain[0], &c.chain[1], &c.trail[0], &c.trail[1]};
+    for (hipEvent_t* e : evs)
+      if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return nullptr;
+    c.ready = true;
+  }
+  return &c;
+}
+
+void launch_trail(hipStream_t st, const HinvWs& w, const double* LT, int d, TrailSpec sp, bool allow128) {
+  auto tiles = [&](int T, TrailSpec& q) -> int64_t {
+    q = sp;
+    const int rows = d - sp.ra0;
+    q.naR = rows > 0 ? (rows + T - 1) / T : 0;
+    if (sp.naC != 0) q.naC = (sp.naC + T - 1) / T;  // naC carries the column count in elements
+    q.nrR = sp.nrR > 0 ? (sp.nrR + T - 1) / T : 0;  // nrR carries the row count in elements
+    const int64_t nA = q.naC == 0 ? int64_t(q.naR) * (q.naR + 1) / 2 : int64_t(q.naR) * q.naC;
+    return nA + int64_t(q.nrR) * (sp.s1 / T);
+  };
+  TrailSpec q;
+  const int64_t n128 = allow128 ? tiles(128, q) : 0;
+  if (allow128 && n128 >= 4 * 256) {
+    hipLaunchKernelGGL(hinv_trail<128>, dim3(unsigned(n128)), dim3(256), 0, st, w.A, w.R, LT, d, q);
+  } else {
+    const int64_t n64 = tiles(64, q);
+    if (n64 > 0) hipLaunchKernelGGL(hinv_trail<64>, dim3(unsigned(n64)), dim3(256), 0, st, w.A, w.R, LT, d, q);
+  }
+}
+
 }  // namespace
 }  // namespace gptq
 
@@ -564,6 +624,15 @@ extern "C" size_t gptq_prepare_hinv_workspace_size(int64_t d) {
   return carve(nullptr, d).bytes;
 }
 
+// Schedule (S = the caller's stream, X = the auxiliary stream). For each
+// super-panel p = [s0, s1), with s2 = s1 + KS:
+//   S: diag/panel steps of p (writing the panel buffer LT[p % 2])
+//   S: wait for X's trailing update of p - 1, then apply p to the next
+//      super-panel's columns [s1, s2) and R rows [s1, s2)   ("trail A")
+//   X: after trail A, apply p to everything at and beyond s2 ("trail B"),
+//      overlapping with the next super-panel's steps on S.
+// The two updates touch disjoint tiles; every pair that touches the same
+// tiles or panel buffer is ordered by an event.
 extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* lambda_out, int32_t* info,
                                  void* ws, size_t ws_bytes, void* stream) {
   if (d < 1 || d > 65536 || H == nullptr || U == nullptr || info == nullptr) return GPTQ_E_INVALID_ARG;
@@ -572,37 +641,53 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
   if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_E_WORKSPACE;
   hipStream_t s = as_stream(stream);
   const int di = int(d);
+  std::lock_guard<std::mutex> lock(g_aux_mu);
+  AuxCtx* ctx = aux_context();
+  hipStream_t x = ctx ? ctx->aux : s;
   hipLaunchKernelGGL(hinv_lambda, dim3(1), dim3(256), 0, s, H, di, damp, w.lam, lambda_out, info);
   const int nb32 = (di + 31) / 32;
   hipLaunchKernelGGL(hinv_setup, dim3(unsigned(nb32 * (nb32 + 1) / 2)), dim3(256), 0, s, H, di, w.lam, w.A);
   const int64_t eye_blocks = (int64_t(di) * di + 511) / 512;
   hipLaunchKernelGGL(hinv_eye, dim3(unsigned(eye_blocks < 4096 ? eye_blocks : 4096)), dim3(256), 0, s, w.R, di);
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
-  for (int s0 = 0; s0 < di; s0 += KS) {
+  if (ctx) {
+    if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(x, ctx->fork, 0) != hipSuccess)
+      return GPTQ_E_HIP;
+  }
+  for (int p = 0, s0 = 0; s0 < di; ++p, s0 += KS) {
     const int s1 = di - s0 < KS ? di : s0 + KS;
+    const double* LTp = w.LT + size_t(p % 2) * KS * di;
+    double* LTw = w.LT + size_t(p % 2) * KS * di;
     for (int k0 = s0; k0 < s1; k0 += NB) {
       const int kb = s1 - k0 < NB ? s1 - k0 : NB;
       const int kl = k0 - s0;
-      hipLaunchKernelGGL(hinv_diag, dim3(1), dim3(256), 0, s, w.A, w.R, w.LT, di, k0, kb, kl, w.Xkk, w.XkkT, info);
+      hipLaunchKernelGGL(hinv_diag, dim3(1), dim3(256), 0, s, w.A, w.R, LTp, di, k0, kb, kl, w.Xkk, w.XkkT, info);
       const int nrow = (di - k0 - kb + 31) / 32;
       const int ncol = k0 / 32;
       if (nrow + ncol > 0)
-        hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, w.LT, di, k0, kb, kl,
+        hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, LTw, di, k0, kb, kl,
                            w.Xkk, w.XkkT, nrow);
     }
     if (s1 < di) {
-      // 128-tiles while there are at least four per CU, 64-tiles below that
-      const int nT = (di - s1 + 127) / 128, nC = s1 / 128;
-      const int64_t n128 = int64_t(nT) * (nT + 1) / 2 + int64_t(nT) * nC;
-      if (n128 >= 4 * 256) {
-        hipLaunchKernelGGL(hinv_trail<128>, dim3(unsigned(n128)), dim3(256), 0, s, w.A, w.R, w.LT, di, s0, s1, nT);
-      } else {
-        const int mT = (di - s1 + 63) / 64, mC = s1 / 64;
-        const int64_t n64 = int64_t(mT) * (mT + 1) / 2 + int64_t(mT) * mC;
-        hipLaunchKernelGGL(hinv_trail<64>, dim3(unsigned(n64)), dim3(256), 0, s, w.A, w.R, w.LT, di, s0, s1, mT);
+      const int s2 = di - s1 < KS ? di : s1 + KS;
+      if (ctx && p >= 1 && hipStreamWaitEvent(s, ctx->trail[(p - 1) % 2], 0) != hipSuccess) return GPTQ_E_HIP;
+      // trail A: columns [s1, s2) of A (all rows below), rows [s1, s2) of R
+      launch_trail(s, w, LTp, di, TrailSpec{s0, s1, s1, 0, s1, s2 - s1, s1, s2 - s1}, false);
+      // trail B: A at and beyond s2 (lower triangle), R rows from s2. It
+      // starts once trail A is done, so that trail A (on the critical path)
+      // has the GPU to itself and trail B overlaps the next panel steps.
+      if (ctx) {
+        if (hipEventRecord(ctx->chain[p % 2], s) != hipSuccess) return GPTQ_E_HIP;
+        if (hipStreamWaitEvent(x, ctx->chain[p % 2], 0) != hipSuccess) return GPTQ_E_HIP;
       }
+      if (s2 < di) launch_trail(x, w, LTp, di, TrailSpec{s0, s1, s2, 0, 0, 0, s2, di - s2}, true);
+      if (ctx && hipEventRecord(ctx->trail[p % 2], x) != hipSuccess) return GPTQ_E_HIP;
     }
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+  }
+  if (ctx) {
+    if (hipEventRecord(ctx->join, x) != hipSuccess || hipStreamWaitEvent(s, ctx->join, 0) != hipSuccess)
+      return GPTQ_E_HIP;
   }
   hipLaunchKernelGGL(hinv_write_u, dim3(2048), dim3(256), 0, s, w.R, di, U);
   return launch_status();
