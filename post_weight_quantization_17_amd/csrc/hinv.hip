@@ -180,14 +180,15 @@ __device__ __forceinline__ double recip(double x) {
 // columns past kb act as identity.
 //
 // Thread t owns the 4x4 block rows 4 (t / 16) .., columns 4 (t % 16) .. in
-// registers for all 64 steps; the 16 threads that hold row j (one quarter of
-// one wave) write it to LDS, double buffered, one barrier per step.
+// registers for all 64 steps; the 16 threads that hold rows j and j+1 (one
+// quarter of one wave) write them to LDS, double buffered, one barrier per
+// two steps.
 __global__ void __launch_bounds__(256)
 hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, int k0, int kb,
           int kl, double* __restrict__ Xkk, double* __restrict__ XkkT, int32_t* __restrict__ info) {
-  __shared__ double Ls[KS - NB][NB];  // Ls[m][i] = L[k0 + i][s0 + m]
+  __shared__ double Ls[KS - NB][NB + 4];  // Ls[m][i] = L[k0 + i][s0 + m]
   __shared__ double T[NB][NB + 1];
-  __shared__ __attribute__((aligned(16))) double bv[2][NB];
+  __shared__ __attribute__((aligned(16))) double bv[2][2][NB];
   const int tid = threadIdx.x, wave = tid >> 6;
   // issue every load first: the diagonal block and the panel rows L_kS'
   constexpr int PER = NB * NB / 256;
@@ -214,7 +215,7 @@ hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __
     zero(acc);
     const int ri[4] = {16 * wave, 16 * wave, 16 * wave, 16 * wave};
     const int cj[4] = {0, 16, 32, 48};
-    blocks_mma<4, true>(acc, &Ls[0][0], NB, &Ls[0][0], NB, ri, cj, kl);
+    blocks_mma<4, true>(acc, &Ls[0][0], NB + 4, &Ls[0][0], NB + 4, ri, cj, kl);
     blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { T[i][j] -= s; });
     __syncthreads();
   }
@@ -230,45 +231,86 @@ hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __
       v[r][c] = in ? t : (i == j ? 1.0 : 0.0);
     }
   double dr[4] = {1.0, 1.0, 1.0, 1.0};
-  // A loop of 16 iterations of 4 unrolled steps: the body stays small
-  // enough to run from the instruction cache (each launch runs it once).
+  // Two steps per barrier: the owners of rows j and j+1 (j even) publish
+  // both rows; every thread applies step j, derives row j+1 after step j at
+  // the positions it needs (its 4 rows, its 4 columns, the pivot pair) with
+  // the same arithmetic the owners use, and applies step j+1. A loop of 16
+  // iterations of 4 unrolled steps keeps the body small enough to run from
+  // the instruction cache (each launch runs it once).
 #pragma nounroll
   for (int jb = 0; jb < NB; jb += 4) {
-    static_for<0, 4>([&](auto jc) {
-      constexpr int jq = decltype(jc)::value;
-      constexpr int b = jq & 1;
-      const int j = jb + jq;
-      if (rb_ == jb) {
-        *reinterpret_cast<double2*>(&bv[b][cb_]) = double2{v[jq][0], v[jq][1]};
-        *reinterpret_cast<double2*>(&bv[b][cb_ + 2]) = double2{v[jq][2], v[jq][3]};
+    static_for<0, 2>([&](auto hc) {
+      constexpr int q0 = 2 * decltype(hc)::value;  // rows jb + q0, jb + q0 + 1
+      constexpr int b = decltype(hc)::value;       // LDS buffer of this round
+      const int j = jb + q0;
+      const bool own_row = rb_ == jb, own_col = cb_ == jb;
+      if (own_row) {
+        *reinterpret_cast<double2*>(&bv[b][0][cb_]) = double2{v[q0][0], v[q0][1]};
+        *reinterpret_cast<double2*>(&bv[b][0][cb_ + 2]) = double2{v[q0][2], v[q0][3]};
+        *reinterpret_cast<double2*>(&bv[b][1][cb_]) = double2{v[q0 + 1][0], v[q0 + 1][1]};
+        *reinterpret_cast<double2*>(&bv[b][1][cb_ + 2]) = double2{v[q0 + 1][2], v[q0 + 1][3]};
       }
       __syncthreads();
-      const double piv = bv[b][j];
-      const double2 r01 = *reinterpret_cast<const double2*>(&bv[b][rb_]);
-      const double2 r23 = *reinterpret_cast<const double2*>(&bv[b][rb_ + 2]);
-      const double2 c01 = *reinterpret_cast<const double2*>(&bv[b][cb_]);
-      const double2 c23 = *reinterpret_cast<const double2*>(&bv[b][cb_ + 2]);
-      const bool own_row = rb_ == jb, own_col = cb_ == jb;
-      dr[jq] = own_row ? piv : dr[jq];
-      const double rp = recip(piv);
-      const double brow[4] = {r01.x, r01.y, r23.x, r23.y};
-      const double bcol[4] = {c01.x, c01.y, c23.x, c23.y};
+      const double pa = bv[b][0][j], pb = bv[b][0][j + 1], pc = bv[b][1][j + 1];
+      double r0[4], c0[4], r1[4], c1[4];
+      {
+        const double2 a01 = *reinterpret_cast<const double2*>(&bv[b][0][rb_]);
+        const double2 a23 = *reinterpret_cast<const double2*>(&bv[b][0][rb_ + 2]);
+        const double2 b01 = *reinterpret_cast<const double2*>(&bv[b][0][cb_]);
+        const double2 b23 = *reinterpret_cast<const double2*>(&bv[b][0][cb_ + 2]);
+        const double2 e01 = *reinterpret_cast<const double2*>(&bv[b][1][rb_]);
+        const double2 e23 = *reinterpret_cast<const double2*>(&bv[b][1][rb_ + 2]);
+        const double2 f01 = *reinterpret_cast<const double2*>(&bv[b][1][cb_]);
+        const double2 f23 = *reinterpret_cast<const double2*>(&bv[b][1][cb_ + 2]);
+        r0[0] = a01.x, r0[1] = a01.y, r0[2] = a23.x, r0[3] = a23.y;
+        c0[0] = b01.x, c0[1] = b01.y, c0[2] = b23.x, c0[3] = b23.y;
+        r1[0] = e01.x, r1[1] = e01.y, r1[2] = e23.x, r1[3] = e23.y;
+        c1[0] = f01.x, c1[1] = f01.y, c1[2] = f23.x, c1[3] = f23.y;
+      }
+      // step j
+      const double rp = recip(pa);
+      dr[q0] = own_row ? pa : dr[q0];
       double m[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m[r] = (rb_ + r > j) ? brow[r] * rp : 0.0;
+      for (int r = 0; r < 4; ++r) m[r] = (rb_ + r > j) ? r0[r] * rp : 0.0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const double nv = fma(-m[r], bcol[c], v[r][c]);
-          if (c == jq) {
-            const double ycol = (r == jq && own_row) ? 1.0 : -m[r];
+          const double nv = fma(-m[r], c0[c], v[r][c]);
+          if (c == q0) {
+            const double ycol = (r == q0 && own_row) ? 1.0 : -m[r];
             v[r][c] = own_col ? ycol : nv;
           } else {
             v[r][c] = nv;
           }
         }
+      // row j+1 after step j: multiplier f = a(j+1, j) / a(j, j); column j
+      // becomes Y's entry -f
+      const double f = pb * rp;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        r1[t] = (rb_ + t == j) ? -f : fma(-f, r0[t], r1[t]);
+        c1[t] = (cb_ + t == j) ? -f : fma(-f, c0[t], c1[t]);
       }
+      const double pc1 = fma(-f, pb, pc);
+      // step j+1
+      const double rp1 = recip(pc1);
+      dr[q0 + 1] = own_row ? pc1 : dr[q0 + 1];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = (rb_ + r > j + 1) ? r1[r] * rp1 : 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const double nv = fma(-m[r], c1[c], v[r][c]);
+          if (c == q0 + 1) {
+            const double ycol = (r == q0 + 1 && own_row) ? 1.0 : -m[r];
+            v[r][c] = own_col ? ycol : nv;
+          } else {
+            v[r][c] = nv;
+          }
+        }
     });
   }
   // The first pivot that is not positive (NaN included) sets `info` to one
@@ -283,8 +325,9 @@ hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __
   }
   __syncthreads();
   if (tid == 0 && bad < NB) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + bad)));
-  // X_kk = D^-1/2 Y: write it row-major and transposed for the panel step,
-  // and into R's diagonal block (zeros above the diagonal).
+  // X_kk = D^-1/2 Y, staged in LDS (T is free again) and written row-major
+  // and transposed for the panel step, and into R's diagonal block (zeros
+  // above the diagonal), all as coalesced rows.
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = rb_ + r;
@@ -292,11 +335,17 @@ hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int j = cb_ + c;
-      const double x = (i < kb && j <= i) ? v[r][c] * si : 0.0;
-      Xkk[i * NB + j] = x;
-      XkkT[j * NB + i] = x;
-      if (i < kb && j < kb) R[int64_t(k0 + i) * d + k0 + j] = x;
+      T[i][j] = (i < kb && j <= i) ? v[r][c] * si : 0.0;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
+    const double x = T[i][j];
+    Xkk[e] = x;
+    XkkT[e] = T[j][i];
+    if (i < kb && j < kb) R[int64_t(k0 + i) * d + k0 + j] = x;
   }
 }
 
@@ -429,14 +478,12 @@ struct TrailSpec {
   int rr0, nrR;   // R part: first row, tile rows (columns: tiles 0 .. s1 / T)
 };
 template <int T>
-__global__ void __launch_bounds__(256, 2)
-hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, TrailSpec sp) {
-  constexpr int TPITCH = T + 4;
+__device__ __forceinline__ void trail_tile(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT,
+                                           int d, const TrailSpec& sp, int tile, double (*As)[T + 4],
+                                           double (*Bs)[T + 4]) {
   constexpr int BL = T / 32;           // 16x16 blocks per wave dimension
   constexpr int STEP = 256 / T;        // k rows loaded per pass
   constexpr int U = TK / STEP;         // loads per thread per chunk and operand
-  __shared__ double As[TK][TPITCH];    // As[k][i] = -L[r0 + i][s0 + k]
-  __shared__ double Bs[TK][TPITCH];    // Bs[k][j] = L[c0 + j][s0 + k] or X[s0 + k][c0 + j]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -445,7 +492,7 @@ hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restr
   const int K = s1 - s0;
   const bool tri = sp.naC == 0;
   const int nA = tri ? sp.naR * (sp.naR + 1) / 2 : sp.naR * sp.naC;
-  int b = blockIdx.x;
+  int b = tile;
   const bool apart = b < nA;
   int r0, c0;
   if (apart) {
@@ -536,6 +583,15 @@ hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restr
         const bool keep = gi < d && (apart ? gj <= gi : gj < s1);
         if (keep) M[int64_t(gi) * d + gj] = acc[ii][jj][r];
       }
+}
+
+// One tile per workgroup.
+template <int T>
+__global__ void __launch_bounds__(256, 2)
+hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, TrailSpec sp) {
+  __shared__ double As[TK][T + 4];  // As[k][i] = -L[r0 + i][s0 + k]
+  __shared__ double Bs[TK][T + 4];  // Bs[k][j] = L[c0 + j][s0 + k] or X[s0 + k][c0 + j]
+  trail_tile<T>(A, R, LT, d, sp, blockIdx.x, As, Bs);
 }
 
 // U[i][j] = X[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -643,6 +699,7 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
   const int di = int(d);
   std::lock_guard<std::mutex> lock(g_aux_mu);
   AuxCtx* ctx = aux_context();
+
   hipStream_t x = ctx ? ctx->aux : s;
   hipLaunchKernelGGL(hinv_lambda, dim3(1), dim3(256), 0, s, H, di, damp, w.lam, lambda_out, info);
   const int nb32 = (di + 31) / 32;
