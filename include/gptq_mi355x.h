@@ -129,6 +129,12 @@ int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* l
  *   group_size -1, or a multiple of 16 with block % group_size == 0 or
  *              group_size % block == 0.
  *   block      128 (the lazy-batch width; other widths -> UNSUPPORTED).
+ *   symmetric  0: the min-max grid above. 1: the symmetric grid (astro-blog
+ *              survey, section 1.2: z = 0, signed values clamped to
+ *              [-2^(bits-1), 2^(bits-1) - 1]; aiqz.cc demo scale): s =
+ *              max|x| / (2^(bits-1) - 1) over the group (max|x| = 1 for an
+ *              all-zero group), stored as code = signed + 2^(bits-1), so
+ *              zeros holds 2^(bits-1). Other values -> INVALID_ARG.
  *   codes      device uint8 d_row x d_col (code per weight).
  *   scales     device fp32 d_row x n_groups, zeros device int32 d_row x
  *              n_groups, n_groups = 1 if group_size == -1 else
@@ -144,9 +150,9 @@ int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* l
 size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int bits,
                                           int64_t group_size, int64_t block);
 int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U,
-                        int bits, int64_t group_size, int64_t block, uint8_t* codes,
-                        float* scales, int32_t* zeros, uint32_t* packed, double* loss,
-                        float* row_loss, void* ws, size_t ws_bytes, void* stream);
+                        int bits, int64_t group_size, int64_t block, int symmetric,
+                        uint8_t* codes, float* scales, int32_t* zeros, uint32_t* packed,
+                        double* loss, float* row_loss, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Packing of existing codes (the same device routine the sweep uses).

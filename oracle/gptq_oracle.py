@@ -42,6 +42,9 @@ the design notes of the repository):
   xmin)/(2^b - 1), z = rint(-xmin/s), code = clamp(rint(x/s) + z, 0, 2^b-1),
   dequant = s (code - z); the range always includes 0 and an all-zero group
   uses [-1, 1]. rint is round-half-to-even.
+* Symmetric variant (optional): z = 0 on the signed grid [-2^(b-1),
+  2^(b-1) - 1] with s = max|x| / (2^(b-1) - 1), stored as the unsigned code
+  signed + 2^(b-1) (so the zero point is the fixed code 2^(b-1)).
 * Group statistics come from the current (already compensated) values when
   the sweep reaches the group's first column; group_size = -1 is one group
   per row taken from the original row.
@@ -146,7 +149,7 @@ def prepare_hinv(H: np.ndarray, damp: float):
 # --------------------------------------------------------------------------
 # Quantizer
 # --------------------------------------------------------------------------
-def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False):
+def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False, symmetric: bool = False):
     """Per-row min-max scale and integer zero of a group of columns.
 
     aiqz.cc, section 分组方案: scale = (max - min)/(2^bits - 1) and the zero
@@ -160,7 +163,26 @@ def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False
     that fixes z (float64, or float32 to match a float32 implementation).
     With ``with_margin`` it also returns how far -xmin/s lay from the nearest
     rounding boundary, in grid steps (0 = an exact tie, 0.5 = an integer).
+
+    ``symmetric``: the signed grid with z = 0 of astro-blog survey, section
+    1.2 (x_q clamped to [-2^(b-1), 2^(b-1) - 1]), with the scale of the
+    aiqz.cc demo (section Python 演示): s = max|x| / (2^(b-1) - 1). Stored
+    as unsigned codes, the signed value plus 2^(b-1), so the zero point is
+    the fixed code 2^(b-1). An all-zero group uses max|x| = 1. The zero is
+    not a rounding decision here, so its margin is reported as 0.5.
     """
+    if symmetric:
+        qs = (1 << (bits - 1)) - 1
+        amax = np.max(np.abs(x), axis=1)
+        amax = np.where(amax == 0.0, 1.0, amax)
+        if decide == F64:
+            s = amax / qs
+        else:
+            s = (amax.astype(decide) / decide(qs)).astype(F64)
+        z = np.full(s.shape, float(1 << (bits - 1)))
+        if with_margin:
+            return s.astype(F64), z, np.full(s.shape, 0.5)
+        return s.astype(F64), z
     maxq = (1 << bits) - 1
     xmin = np.minimum(np.min(x, axis=1), 0.0)
     xmax = np.maximum(np.max(x, axis=1), 0.0)
@@ -198,7 +220,7 @@ def quantize_codes(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decid
     return c
 
 
-def rtn(W: np.ndarray, bits: int, group_size: int):
+def rtn(W: np.ndarray, bits: int, group_size: int, symmetric: bool = False):
     """Round-to-nearest baseline: every weight rounded on its own group grid.
 
     aiqz.cc, section Python 演示 (the round-only baseline) and xuzou.cn,
@@ -215,7 +237,7 @@ def rtn(W: np.ndarray, bits: int, group_size: int):
     zeros = np.zeros((d_row, n_groups))
     for k in range(n_groups):
         sl = slice(k * g, min(d_col, (k + 1) * g))
-        s, z = group_params(W[:, sl], bits)
+        s, z = group_params(W[:, sl], bits, symmetric=symmetric)
         scales[:, k], zeros[:, k] = s, z
         codes[:, sl] = quantize_codes(W[:, sl], s[:, None], z[:, None], bits)
     return codes.astype(np.uint8), scales, zeros
@@ -242,6 +264,7 @@ def quantize_layer(
     group_size: int,
     block: int = 128,
     decide=F64,
+    symmetric: bool = False,
 ):
     """GPTQ sweep of one layer, columns in natural order.
 
@@ -265,7 +288,8 @@ def quantize_layer(
     -xmin/s when the zero point was chosen).
     ``decide`` is the precision in which each code is decided (float64 by
     default; float32 reproduces the decision of a float32 implementation
-    given the same inputs).
+    given the same inputs). ``symmetric`` selects the symmetric grid of
+    ``group_params``.
     """
     W = np.array(W, dtype=F64, copy=True)
     U = np.asarray(U, dtype=F64)
@@ -289,7 +313,7 @@ def quantize_layer(
     zero_margin = np.zeros((d_row, n_groups))
 
     if group_size == -1 and d_col:
-        s, z, zm = group_params(W, bits, decide, with_margin=True)
+        s, z, zm = group_params(W, bits, decide, with_margin=True, symmetric=symmetric)
         scales[:, 0], zeros[:, 0], zero_margin[:, 0] = s, z, zm
 
     for i1 in range(0, d_col, block):
@@ -298,7 +322,9 @@ def quantize_layer(
         for q in range(i1, i2):
             if group_size != -1 and q % group_size == 0:
                 k = q // group_size
-                s, z, zm = group_params(W[:, q : min(q + group_size, d_col)], bits, decide, with_margin=True)
+                s, z, zm = group_params(
+                    W[:, q : min(q + group_size, d_col)], bits, decide, with_margin=True, symmetric=symmetric
+                )
                 scales[:, k], zeros[:, k], zero_margin[:, k] = s, z, zm
             w = W[:, q]
             c, code_margin[:, q] = quantize_codes(w, s, z, bits, decide, with_margin=True)

@@ -37,7 +37,7 @@ _SIGNATURES = {
     "gptq_quantize_layer_workspace_size": (_c_size, [_c_i64, _c_i64, _c_int, _c_i64, _c_i64]),
     "gptq_quantize_layer": (
         _c_int,
-        [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr],
+        [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr],
     ),
     "gptq_pack_codes": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr]),
 }
@@ -210,8 +210,10 @@ def gptq_quantize_layer(
     want_row_loss: bool = True,
     ws: Optional[torch.Tensor] = None,
     out: Optional[Quantized] = None,
+    symmetric: bool = False,
 ) -> Quantized:
-    """GPTQ sweep of W [d_row, d_col] (fp16/fp32) with the factor U."""
+    """GPTQ sweep of W [d_row, d_col] (fp16/fp32) with the factor U
+    (min-max grid, or the symmetric grid with ``symmetric``)."""
     _on_gpu("W", W)
     _on_gpu("U", U)
     if W.dim() != 2 or not W.is_contiguous():
@@ -235,7 +237,7 @@ def gptq_quantize_layer(
     _check(
         "gptq_quantize_layer",
         lib.gptq_quantize_layer(
-            _ptr(W), _dtype_code(W), d_row, d_col, _ptr(U), bits, group_size, block,
+            _ptr(W), _dtype_code(W), d_row, d_col, _ptr(U), bits, group_size, block, int(bool(symmetric)),
             _ptr(out.codes), _ptr(out.scales), _ptr(out.zeros), _ptr(out.packed), _ptr(out.loss),
             _ptr(out.row_loss), _ptr(ws), ws.numel(), _stream(),
         ),

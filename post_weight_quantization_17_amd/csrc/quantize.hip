@@ -63,15 +63,27 @@ __device__ __forceinline__ floatx4 load4(const __half* p) {
   return floatx4{__low2float(a), __high2float(a), __low2float(b), __high2float(b)};
 }
 
-// Min-max grid of one group: the range always includes 0; an all-zero group
-// uses [-1, 1]. s = (xmax - xmin)/maxq, z = rint(-xmin/s).
-__device__ __forceinline__ void grid_params(float mn, float mx, float maxq, float& s, float& z, float& rs) {
-  if (mn == 0.f && mx == 0.f) {
-    mn = -1.f;
-    mx = 1.f;
+// Grid of one group from its range [mn, mx] (which always includes 0).
+// Min-max (astro-blog survey, 1.2; aiqz.cc, 分组方案): an all-zero group uses
+// [-1, 1]; s = (xmax - xmin)/maxq, z = rint(-xmin/s).
+// Symmetric (astro-blog survey, 1.2 with the aiqz.cc demo's scale): z = 0 on
+// the signed grid, stored as unsigned codes with zero point zs = 2^(b-1);
+// s = max|x| / qs, qs = 2^(b-1) - 1; an all-zero group uses max|x| = 1.
+__device__ __forceinline__ void grid_params(float mn, float mx, float maxq, int sym, float qs, float zs, float& s,
+                                            float& z, float& rs) {
+  if (sym) {
+    float amax = fmaxf(-mn, mx);
+    if (amax == 0.f) amax = 1.f;
+    s = amax / qs;
+    z = zs;
+  } else {
+    if (mn == 0.f && mx == 0.f) {
+      mn = -1.f;
+      mx = 1.f;
+    }
+    s = (mx - mn) / maxq;
+    z = rintf(-mn / s);
   }
-  s = (mx - mn) / maxq;
-  z = rintf(-mn / s);
   rs = 1.f / s;
 }
 
@@ -152,7 +164,7 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
 template <typename WT, bool WHOLE>
 __global__ void __launch_bounds__(QT, 2)
 gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __restrict__ U, int d_row, int d_col,
-           int bits, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
+           int bits, int sym, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
            int32_t* __restrict__ zeros, uint32_t* __restrict__ packed, int nwords, float* __restrict__ row_loss,
            double* __restrict__ wg_loss) {
   __shared__ __attribute__((aligned(16))) float Ud[QB][QB];
@@ -168,6 +180,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
   const bool row_ok = row < d_row;
   const size_t rbase = size_t(row) * d_col;
   const float maxq = float((1 << bits) - 1);
+  const float qs = float((1 << (bits - 1)) - 1), zs = float(1 << (bits - 1));
 
   float s = 1.f, z = 0.f, rs = 1.f;
   double lacc = 0.0;
@@ -182,7 +195,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       }
     mn = row16_min(mn);
     mx = row16_max(mx);
-    grid_params(mn, mx, maxq, s, z, rs);
+    grid_params(mn, mx, maxq, sym, qs, zs, s, z, rs);
     if (sub == 0 && row_ok) {
       scales[row] = s;
       zeros[row] = int(z);
@@ -274,7 +287,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
           }
           mn = row16_min(mn);
           mx = row16_max(mx);
-          grid_params(mn, mx, maxq, s, z, rs);
+          grid_params(mn, mx, maxq, sym, qs, zs, s, z, rs);
           if (sub == 0 && row_ok) {
             const int g = (i1 + q) / group;
             scales[size_t(row) * ngroups + g] = s;
@@ -461,14 +474,14 @@ extern "C" size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_co
 }
 
 extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U, int bits,
-                                   int64_t group_size, int64_t block, uint8_t* codes, float* scales, int32_t* zeros,
-                                   uint32_t* packed, double* loss, float* row_loss, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   int64_t group_size, int64_t block, int symmetric, uint8_t* codes, float* scales,
+                                   int32_t* zeros, uint32_t* packed, double* loss, float* row_loss, void* ws,
+                                   size_t ws_bytes, void* stream) {
   if (d_row < 1 || d_col < 1 || d_row > (int64_t(1) << 30) || d_col > (1 << 20)) return GPTQ_E_INVALID_ARG;
   if (d_row * d_col > (int64_t(1) << 40)) return GPTQ_E_INVALID_ARG;
   if (!W || !U || !codes || !scales || !zeros || !packed || !loss) return GPTQ_E_INVALID_ARG;
   if (wdtype != GPTQ_F16 && wdtype != GPTQ_F32) return GPTQ_E_INVALID_ARG;
-  if (!bits_ok(bits)) return GPTQ_E_INVALID_ARG;
+  if (!bits_ok(bits) || (symmetric != 0 && symmetric != 1)) return GPTQ_E_INVALID_ARG;
   if (block < 1) return GPTQ_E_INVALID_ARG;
   if (group_size != -1) {
     if (group_size < 1 || (block % group_size != 0 && group_size % block != 0)) return GPTQ_E_INVALID_ARG;
@@ -490,12 +503,12 @@ extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int
   if (wdtype == GPTQ_F16) {
     auto k = whole ? gptq_sweep<__half, true> : gptq_sweep<__half, false>;
     hipLaunchKernelGGL(k, dim3(nwg), dim3(QT), 0, s, static_cast<const __half*>(W), w.Wf, U, int(d_row), int(d_col),
-                       bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
+                       bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
                        w.wg_loss);
   } else {
     auto k = whole ? gptq_sweep<float, true> : gptq_sweep<float, false>;
     hipLaunchKernelGGL(k, dim3(nwg), dim3(QT), 0, s, static_cast<const float*>(W), w.Wf, U, int(d_row), int(d_col),
-                       bits, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
+                       bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
                        w.wg_loss);
   }
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;

@@ -214,6 +214,40 @@ def test_identity_hessian_is_rtn_bit_exact(gpu, bits, group):
     assert np.allclose(q.scales.cpu().numpy(), ref["scales"], rtol=1e-7)
 
 
+SYM_CASES = [
+    (16, 128, 4, 128, np.float16),
+    (33, 200, 3, 32, np.float16),
+    (20, 300, 2, 64, np.float32),
+    (64, 256, 3, 128, np.float16),
+    (64, 640, 8, -1, np.float16),
+]
+
+
+@pytest.mark.parametrize("d_row,d_col,bits,group,wdt", SYM_CASES)
+def test_quantize_layer_parity_symmetric(gpu, d_row, d_col, bits, group, wdt):
+    say("sweep symmetric", d_row, d_col, bits, group, wdt.__name__)
+    U = oracle_u(d_col, d_col + 2 * bits)
+    W = (0.02 * np.random.default_rng(3 * d_row + d_col).standard_normal((d_row, d_col))).astype(wdt)
+    q = gpu.gptq_quantize_layer(gpu_tensor(W), gpu_tensor(U), bits, group, 128, symmetric=True)
+    torch.cuda.synchronize()
+    ref = O.quantize_layer(W, U, bits, group, 128, decide=np.float32, symmetric=True)
+    check_quant(q, ref, bits)
+    assert np.all(q.zeros.cpu().numpy() == 2 ** (bits - 1))
+
+
+@pytest.mark.parametrize("bits,group", [(4, -1), (3, 128), (2, 32), (8, 16)])
+def test_identity_hessian_symmetric_is_rtn_bit_exact(gpu, bits, group):
+    d_col = 384
+    W = (0.02 * np.random.default_rng(10 + bits).standard_normal((40, d_col))).astype(np.float32)
+    U = (np.eye(d_col) / np.sqrt(1.01)).astype(np.float32)
+    q = gpu.gptq_quantize_layer(gpu_tensor(W), gpu_tensor(U), bits, group, 128, symmetric=True)
+    torch.cuda.synchronize()
+    ref = O.quantize_layer(W, U, bits, group, 128, decide=np.float32, symmetric=True)
+    assert np.array_equal(q.codes.cpu().numpy(), ref["codes"])
+    assert np.array_equal(q.zeros.cpu().numpy(), ref["zeros"].astype(np.int32))
+    assert np.allclose(q.scales.cpu().numpy(), ref["scales"], rtol=1e-7)
+
+
 def test_quantize_is_deterministic(gpu):
     U = gpu_tensor(oracle_u(384, 3))
     W = gpu_tensor((0.02 * np.random.default_rng(9).standard_normal((80, 384))).astype(np.float16))
@@ -257,6 +291,10 @@ def test_abi_rejects_bad_arguments(gpu):
     st = lib.gptq_hessian_accumulate(X.data_ptr(), 0, 8, 16, 16, H.data_ptr(), 0, ws.data_ptr(), 16, None)
     assert st == gpu.GPTQ_E_WORKSPACE
     st = lib.gptq_hessian_accumulate(X.data_ptr(), 0, 8, 16, 8, H.data_ptr(), 0, ws.data_ptr(), 16, None)
+    assert st == gpu.GPTQ_E_INVALID_ARG
+    # symmetric must be 0 or 1 (checked before any launch or output access)
+    st = lib.gptq_quantize_layer(W.data_ptr(), 0, 4, 64, U.data_ptr(), 4, -1, 128, 2, H.data_ptr(), H.data_ptr(),
+                                 H.data_ptr(), H.data_ptr(), H.data_ptr(), None, ws.data_ptr(), 16, None)
     assert st == gpu.GPTQ_E_INVALID_ARG
 
 

@@ -128,6 +128,59 @@ def test_identity_hessian_reduces_to_rtn(bits, group):
     assert out["loss"] == pytest.approx(0.5 * (1 + lam) * np.sum((W - what) ** 2), rel=1e-12)
 
 
+def _demo_nearest_quant(w, bits):
+    # Round-to-nearest of the aiqz.cc demo (section Python 演示), written out
+    # here on its own: scale = max|w| / qmax, clip(round(w / scale), -qmax,
+    # qmax) * scale, qmax = 2^(b-1) - 1.
+    qmax = 2 ** (bits - 1) - 1
+    scale = np.abs(w).max() / qmax
+    return np.clip(np.round(w / scale), -qmax, qmax) * scale
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("group", [-1, 16])
+def test_symmetric_identity_hessian_is_demo_rounding(bits, group):
+    W = 0.02 * rng(40 + bits).standard_normal((6, 32))
+    U, _ = O.prepare_hinv(np.eye(32), 0.0)  # U = I: nothing is compensated
+    out = O.quantize_layer(W, U, bits, group, block=8, symmetric=True)
+    g = 32 if group == -1 else group
+    ref = np.hstack([np.vstack([_demo_nearest_quant(r, bits) for r in W[:, k : k + g]]) for k in range(0, 32, g)])
+    assert np.array_equal(out["Wq"], ref)
+    assert np.all(out["zeros"] == 2 ** (bits - 1))
+
+
+def test_symmetric_hand_example():
+    # 3 bits: qmax = 3, s = 0.6 / 3 = 0.2, zero code 4. U = I.
+    #   0.6 / 0.2 = 3 -> code 7; -0.25 / 0.2 = -1.25 -> -1 -> code 3;
+    #   0.13 / 0.2 = 0.65 -> 1 -> code 5; 0 -> code 4
+    U, _ = O.prepare_hinv(np.eye(4), 0.0)
+    out = O.quantize_layer(np.array([[0.6, -0.25, 0.13, 0.0]]), U, 3, -1, block=128, symmetric=True)
+    assert out["codes"].tolist() == [[7, 3, 5, 4]]
+    assert out["scales"][0, 0] == pytest.approx(0.2, rel=1e-15) and out["zeros"][0, 0] == 4
+
+
+@pytest.mark.parametrize("bits,group", [(4, -1), (3, 16), (2, 32)])
+def test_symmetric_blocked_equals_unblocked_and_on_grid(bits, group):
+    _, W, _, U, _ = sweep_case(5, 64, 400, 21)
+    ref = O.quantize_layer(W, U, bits, group, block=1, symmetric=True)
+    for B in (8, 32, 64):
+        out = O.quantize_layer(W, U, bits, group, block=B, symmetric=True)
+        assert np.array_equal(out["codes"], ref["codes"])
+        assert np.allclose(out["Wq"], ref["Wq"], rtol=0, atol=1e-12)
+    g = 64 if group == -1 else group
+    sc = np.repeat(ref["scales"], g, axis=1)[:, :64]
+    t = ref["Wq"] / sc + 2 ** (bits - 1)
+    assert np.allclose(t, np.rint(t), atol=1e-9) and t.min() >= -1e-9 and t.max() <= 2**bits - 1 + 1e-9
+
+
+def test_symmetric_gptq_beats_symmetric_rtn():
+    X, W, H, U, lam = sweep_case(12, 48, 300, 5)
+    out = O.quantize_layer(W, U, 3, -1, symmetric=True)
+    codes, scales, zeros = O.rtn(W, 3, -1, symmetric=True)
+    rtn_loss = O.layer_loss_direct(X, W, O.dequantize(codes, scales, zeros, -1), lam)
+    assert out["loss"] < rtn_loss
+
+
 def test_decision_margins():
     # w/s = 2.5 (exact tie), 3.0, 2.4, -0.75 -> distance to the nearest
     # rounding boundary 0, 0.5, 0.1, 0.25 grid steps
