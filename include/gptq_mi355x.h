@@ -155,6 +155,38 @@ int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col,
                         double* loss, float* row_loss, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Use of the packed layer: quantized matrix x full-precision vectors.
+ *
+ * Defines: xuzou.cn reading card of the GPTQ paper, section 方法适配 (last
+ * paragraph) and section 瓶颈: the inference kernel multiplies the
+ * quantized matrix by full-precision activation vectors and dequantizes the
+ * weights on the fly, so that batch-1 generation reads the low-bit words.
+ * Dequantization What = s (code - z) per group (astro-blog survey, section
+ * 1.2). For b < batch, r < d_row:
+ *   y[b][r] = sum_c x[b][c] * scales[r][g(c)] * (code[r][c] - zeros[r][g(c)])
+ * with code[r][c] read from `packed` (layout of gptq_quantize_layer) and
+ * g(c) = c / group_size (0 if group_size == -1).
+ *   packed     device uint32 d_row x ceil(d_col * bits / 32).
+ *   scales     device fp32, zeros device int32, d_row x n_groups.
+ *   bits       2, 3, 4 or 8.
+ *   group_size -1, or a multiple of 8.
+ *   x          device fp16, batch rows of d_col values, row stride ldx >= d_col.
+ *   y          device fp32, batch x d_row, row-major.
+ * fp32 accumulation of exact codes times fp16 activations; the per-row sum
+ * over lanes has a fixed order, so results are deterministic. When
+ * group_size is -1 or a multiple of 32 and x rows are 16-byte aligned
+ * (ldx % 8 == 0, x 16-byte aligned), a faster kernel runs (two codes per
+ * instruction, several rows per wave); other layouts take a per-code
+ * kernel. Runs on `stream` (NULL: the default stream); nothing is
+ * allocated. Errors: sizes < 1, NULL pointers, ldx < d_col, bad bits or
+ * group -> GPTQ_E_INVALID_ARG; a failed launch or device query ->
+ * GPTQ_E_HIP.
+ * ---------------------------------------------------------------------- */
+int gptq_dequant_matvec(const uint32_t* packed, const float* scales, const int32_t* zeros,
+                        int64_t d_row, int64_t d_col, int bits, int64_t group_size, const void* x,
+                        int64_t batch, int64_t ldx, float* y, void* stream);
+
+/* ------------------------------------------------------------------------
  * Packing of existing codes (the same device routine the sweep uses).
  *
  * Defines: b-bit codes stored in 32-bit integer arrays (mcipr.com

@@ -400,3 +400,25 @@ def unpack(words: np.ndarray, d_col: int, bits: int) -> np.ndarray:
     stream = stream[:, : d_col * bits].reshape(d_row, d_col, bits)
     vals = (stream << np.arange(bits, dtype=np.uint64)).sum(axis=2)
     return vals.astype(np.uint8)
+
+
+# --------------------------------------------------------------------------
+# Use of the packed layer: quantized matrix x full-precision vector
+# --------------------------------------------------------------------------
+def dequant_matvec(packed: np.ndarray, scales: np.ndarray, zeros: np.ndarray, d_col: int, bits: int,
+                   group_size: int, x: np.ndarray) -> np.ndarray:
+    """Y = X What^T with What decoded from the packed words.
+
+    xuzou.cn reading card, section 方法适配 (last paragraph) and section 瓶颈:
+    inference multiplies the quantized matrix by full-precision activation
+    vectors, dequantizing the weights on the fly, so that batch-1 generation
+    reads the low-bit words instead of fp16 weights. What = s (code - z) per
+    group (astro-blog survey, section 1.2).
+
+    ``packed`` [d_row, words_per_row], ``scales``/``zeros`` [d_row, n_groups],
+    ``x`` [batch, d_col] (any float dtype, upcast exactly). Returns
+    [batch, d_row] in float64.
+    """
+    codes = unpack(packed, d_col, bits)
+    What = dequantize(codes, scales, zeros, group_size)
+    return np.asarray(x, dtype=F64) @ What.T

@@ -40,6 +40,10 @@ _SIGNATURES = {
         [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr],
     ),
     "gptq_pack_codes": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr]),
+    "gptq_dequant_matvec": (
+        _c_int,
+        [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr],
+    ),
 }
 
 
@@ -255,3 +259,46 @@ def gptq_pack_codes(codes: torch.Tensor, bits: int, packed: Optional[torch.Tenso
         packed = torch.empty((d_row, words_per_row(d_col, bits)), dtype=torch.int32, device=codes.device)
     _check("gptq_pack_codes", load().gptq_pack_codes(_ptr(codes), d_row, d_col, bits, _ptr(packed), _stream()))
     return packed
+
+
+# ------------------------------------------------------------ packed use
+def gptq_dequant_matvec(
+    packed: torch.Tensor,
+    scales: torch.Tensor,
+    zeros: torch.Tensor,
+    d_col: int,
+    bits: int,
+    group_size: int,
+    x: torch.Tensor,
+    y: Optional[torch.Tensor] = None,
+) -> torch.Tensor:
+    """y [batch, d_row] = x [batch, d_col] (fp16) times the dequantized
+    packed matrix, transposed."""
+    for name, t in (("packed", packed), ("scales", scales), ("zeros", zeros), ("x", x)):
+        _on_gpu(name, t)
+    if x.dtype != torch.float16 or x.dim() not in (1, 2) or x.stride(-1) != 1:
+        raise ValueError("x must be a float16 [d_col] or [batch, d_col] tensor with unit column stride")
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    batch = x2.shape[0]
+    if x2.shape[1] != d_col:
+        raise ValueError("x has the wrong width")
+    d_row = packed.shape[0]
+    if (packed.shape[1] != words_per_row(d_col, bits) or not packed.is_contiguous()
+            or packed.dtype not in (torch.int32, torch.uint32)):
+        raise ValueError("packed must be a contiguous [d_row, words_per_row] 32-bit tensor")
+    ng = n_groups(d_col, group_size) if group_size == -1 or group_size > 0 else 1
+    if scales.shape != (d_row, ng) or scales.dtype != torch.float32 or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous float32 [d_row, n_groups] tensor")
+    if zeros.shape != (d_row, ng) or zeros.dtype != torch.int32 or not zeros.is_contiguous():
+        raise ValueError("zeros must be a contiguous int32 [d_row, n_groups] tensor")
+    if y is None:
+        y = torch.empty((batch, d_row), dtype=torch.float32, device=x.device)
+    ldx = x2.stride(0) if batch > 1 else d_col
+    _check(
+        "gptq_dequant_matvec",
+        load().gptq_dequant_matvec(
+            _ptr(packed), _ptr(scales), _ptr(zeros), d_row, d_col, bits, group_size, _ptr(x2), batch, ldx,
+            _ptr(y), _stream(),
+        ),
+    )
+    return y.squeeze(0) if x.dim() == 1 else y

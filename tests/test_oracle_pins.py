@@ -181,6 +181,29 @@ def test_symmetric_gptq_beats_symmetric_rtn():
     assert out["loss"] < rtn_loss
 
 
+def test_dequant_matvec_hand_example():
+    # 2 rows, 3 columns, 4-bit, one group per row:
+    #   row 0: s = 0.5, z = 8, codes [9, 7, 8] -> What [0.5, -0.5, 0]
+    #   row 1: s = 2,   z = 1, codes [3, 1, 0] -> What [4, 0, -2]
+    #   x = [[1, 2, 3], [0, 0, 1]] -> Y = [[-0.5, -2], [0, -2]]
+    codes = np.array([[9, 7, 8], [3, 1, 0]])
+    packed = O.pack(codes, 4)
+    scales = np.array([[0.5], [2.0]])
+    zeros = np.array([[8.0], [1.0]])
+    y = O.dequant_matvec(packed, scales, zeros, 3, 4, -1, np.array([[1.0, 2.0, 3.0], [0.0, 0.0, 1.0]]))
+    assert y.tolist() == [[-0.5, -2.0], [0.0, -2.0]]
+
+
+@pytest.mark.parametrize("bits,group", [(3, 16), (4, 32), (2, -1), (8, 16)])
+def test_dequant_matvec_unit_vectors_read_the_dequantized_columns(bits, group):
+    # e_c picks column c of What = s (code - z); checked against the sweep's
+    # own dequantized weights (Wq), which the on-grid pin ties to the codes.
+    _, W, _, U, _ = sweep_case(3, 48, 200, 31)
+    out = O.quantize_layer(W, U, bits, group, block=16)
+    y = O.dequant_matvec(out["packed"], out["scales"], out["zeros"], 48, bits, group, np.eye(48))
+    assert np.allclose(y.T, out["Wq"], rtol=0, atol=1e-15)
+
+
 def test_decision_margins():
     # w/s = 2.5 (exact tie), 3.0, 2.4, -0.75 -> distance to the nearest
     # rounding boundary 0, 0.5, 0.1, 0.25 grid steps
