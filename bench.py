@@ -181,7 +181,9 @@ def matvec_measure(g, torch, q, W, cfg, reps=50, replays=10):
         "frac_hbm": nbytes / (us * 1e-6) / PEAK_HBM,
         "fp16_dense_us": dense_us,
         "fp16_dense_bytes": Wh.numel() * 2,
-        "kernel": "dequant_matvec_kernel (gptq_dequant_matvec), timed by HIP graph replay",
+        "kernel": (
+            "dequant_matvec_pairs" if cfg.group_size == -1 or cfg.group_size % 32 == 0 else "dequant_matvec_kernel"
+        ) + " (gptq_dequant_matvec), timed by HIP graph replay",
     }
 
 

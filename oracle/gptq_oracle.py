@@ -51,6 +51,16 @@ the design notes of the repository):
 * Blocks are exact: after a block, W[:, i2:] -= E U[i1:i2, i2:] applies the
   deferred rank-1 updates, so any block size gives the same numbers up to
   rounding. Grouping needs block % group == 0 or group % block == 0.
+* Act-order (the `desc_act` flag of the library configuration the
+  mcipr.com page shows, section 四; the page gives no definition): columns
+  are quantized in order of descending diag(H) (ties by ascending column
+  index, NaN last), which is the method above run on W[:, p] and
+  H[p][:, p]; groups are consecutive in that order, so group statistics
+  follow the permuted order.
+* The greedy order (astro-blog survey, section 2.2, OBQ) is a slow
+  reference: per row, repeatedly the free weight with the least
+  (w - quant(w))^2 / [H_F^-1]_qq, with the inverse of the free sub-Hessian
+  kept by Gaussian elimination; one grid per row from the original row.
 * Packing: per row, an LSB-first bitstream along the columns; code j fills
   bits [b j, b j + b) and word k holds bits [32 k, 32 k + 32); rows are
   zero-padded to ceil(d_col b / 32) words.
@@ -351,6 +361,119 @@ def quantize_layer(
         code_margin=code_margin,
         zero_margin=zero_margin,
     )
+
+
+# --------------------------------------------------------------------------
+# Column orders: act-order, and the greedy order of OBQ (slow reference)
+# --------------------------------------------------------------------------
+def act_order_perm(H: np.ndarray) -> np.ndarray:
+    """Column order by descending diag(H): p[q] is the original column taken
+    q-th. Equal values keep ascending column order; NaN values come last (in
+    ascending column order); -0 equals +0.
+
+    mcipr.com "一文读懂GPTQ", section 四 (the `desc_act` flag of the library
+    configuration); the order itself is the reading stated in this module's
+    header.
+    """
+    h = np.diag(np.asarray(H, dtype=F64))
+
+    def key(i):
+        v = h[i]
+        return (1, 0.0, i) if np.isnan(v) else (0, -v, i)
+
+    return np.array(sorted(range(h.shape[0]), key=key), dtype=np.int64)
+
+
+def inverse_perm(p: np.ndarray) -> np.ndarray:
+    """inv[p[q]] = q."""
+    p = np.asarray(p, dtype=np.int64)
+    inv = np.empty_like(p)
+    inv[p] = np.arange(p.shape[0])
+    return inv
+
+
+def quantize_layer_act_order(
+    W: np.ndarray,
+    H: np.ndarray,
+    bits: int,
+    group_size: int,
+    block: int = 128,
+    damp: float = 0.01,
+    decide=F64,
+    symmetric: bool = False,
+):
+    """The layer quantized in act-order: the fixed-order method on the
+    columns of W taken in the order p = act_order_perm(H), with the
+    Hessian's rows and columns taken in the same order. Returns the dict of
+    ``quantize_layer`` (codes, scales, zeros, Wq, packed, ... all in the
+    permuted column order, groups consecutive in that order) plus ``perm``,
+    ``lam``, ``U`` (the factor of the permuted Hessian), ``Wq_orig`` (the
+    dequantized weights back in the original column order) and ``g_idx``
+    (group of each original column).
+    """
+    H = np.asarray(H, dtype=F64)
+    p = act_order_perm(H)
+    U, lam = prepare_hinv(H[np.ix_(p, p)], damp)
+    r = quantize_layer(np.asarray(W)[:, p], U, bits, group_size, block, decide, symmetric)
+    inv = inverse_perm(p)
+    r.update(
+        perm=p,
+        lam=lam,
+        U=U,
+        Wq_orig=r["Wq"][:, inv],
+        g_idx=np.zeros(p.shape[0], dtype=np.int64) if group_size == -1 else inv // group_size,
+    )
+    return r
+
+
+def obq_greedy(W: np.ndarray, H: np.ndarray, bits: int, damp: float = 0.01, decide=F64, order=None):
+    """OBQ, one row at a time (astro-blog survey, section 2.2): among the
+    free weights F of the row, quantize the one with the least
+    (w_q - quant(w_q))^2 / [H_F^-1]_qq, then correct the free weights by the
+    OBS step w_F -= (w_q - quant(w_q)) / [H_F^-1]_qq * [H_F^-1]_{F,q} and
+    drop q from the inverse by one Gaussian elimination step,
+    H_F'^-1 = H_F^-1 - H_F^-1[:, q] H_F^-1[q, :] / [H_F^-1]_qq. Ties go to
+    the lowest column index. ``order`` (optional) fixes the order instead of
+    the greedy choice. The grid is one per row from the original row
+    (``group_params``), the Hessian is damped as in ``damped``.
+
+    Returns codes, Wq, row_loss, loss (sum of err^2 / (2 [H_F^-1]_qq)) and
+    the order taken per row [d_row, d_col].
+    """
+    W = np.asarray(W, dtype=F64)
+    d_row, d_col = W.shape
+    H_d, _ = damped(np.asarray(H, dtype=F64), damp)
+    Hinv0 = np.linalg.inv(H_d)
+    codes = np.zeros((d_row, d_col), dtype=np.uint8)
+    Wq = np.zeros((d_row, d_col))
+    row_loss = np.zeros(d_row)
+    taken = np.zeros((d_row, d_col), dtype=np.int64)
+    for r in range(d_row):
+        s, z = group_params(W[r : r + 1], bits, decide)
+        w = W[r].copy()
+        Hinv = Hinv0.copy()
+        free = np.ones(d_col, dtype=bool)
+        for step in range(d_col):
+            if order is None:
+                idx = np.flatnonzero(free)
+                c = quantize_codes(w[idx], np.full(idx.shape, s[0]), np.full(idx.shape, z[0]), bits, decide)
+                cost = (w[idx] - s[0] * (c - z[0])) ** 2 / np.diag(Hinv)[idx]
+                q = int(idx[int(np.argmin(cost))])
+            else:
+                q = int(order[step])
+            c = quantize_codes(w[q : q + 1], s, z, bits, decide)[0]
+            what = s[0] * (c - z[0])
+            err = w[q] - what
+            dq = Hinv[q, q]
+            row_loss[r] += err * err / (2.0 * dq)
+            w[free] -= (err / dq) * Hinv[free, q]
+            Hinv = Hinv - np.outer(Hinv[:, q], Hinv[q, :]) / dq
+            free[q] = False
+            w[q] = what
+            codes[r, q] = c
+            Wq[r, q] = what
+            taken[r, step] = q
+    return dict(codes=codes, Wq=Wq, row_loss=row_loss, loss=float(np.sum(row_loss)), order=taken)
 
 
 def layer_loss_direct(X: np.ndarray, W: np.ndarray, Wq: np.ndarray, lam: float = 0.0) -> float:
