@@ -155,6 +155,49 @@ int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col,
                         double* loss, float* row_loss, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Column order: act-order permutation.
+ *
+ * Defines: mcipr.com "一文读懂GPTQ", section 四 (the desc_act flag of the
+ * method's library configuration; the page gives no formula). Reading: the
+ * columns are quantized in order of descending diag(H); equal values keep
+ * ascending column order, NaN values come last, -0 equals +0. The layer is
+ * then the fixed-order method on W[:, perm] with H[perm][:, perm] (gather
+ * both with gptq_gather, then gptq_prepare_hinv and gptq_quantize_layer);
+ * groups are consecutive in the permuted order, so group k of the outputs
+ * covers the original columns perm[k g .. k g + g - 1].
+ *   H        device fp32, d x d, row stride ldh >= d; only the diagonal is read.
+ *   perm     device int32 [d]: perm[q] = original column quantized q-th.
+ *   invperm  device int32 [d]: invperm[perm[q]] = q (also the rank buffer).
+ * Runs on `stream`; nothing is allocated. Errors: d < 1, d > 2^27, ldh < d,
+ * NULL pointers -> GPTQ_E_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+int gptq_act_order_perm(const float* H, int64_t d, int64_t ldh, int32_t* perm, int32_t* invperm,
+                        void* stream);
+
+/* ------------------------------------------------------------------------
+ * Row and column gather (moves a layer into or out of a column order).
+ *
+ * Defines: the permuted layer of the act-order reading above (mcipr.com
+ * "一文读懂GPTQ", section 四): W[:, perm], H[perm][:, perm], the codes back
+ * in original order (codes_p[:, invperm]) and activations in the permuted
+ * order (x[:, perm]) for the packed product.
+ *   dst[i][q] = src[row_idx[i]][col_idx[q]], i < rows, q < cols; a NULL
+ *   index array means the identity.
+ *   src      device, src_rows x src_cols elements of elem_bytes (1, 2 or 4)
+ *            bytes, row stride ld_src >= src_cols (elements).
+ *   dst      device, rows x cols, row stride ld_dst >= cols; must not
+ *            overlap src.
+ *   info     device int32 or NULL: set to 0, then to 1 if any index lies
+ *            outside the source; such elements are written as 0.
+ * Runs on `stream`; nothing is allocated. Errors: sizes < 1, NULL src or
+ * dst, ld_src < src_cols, ld_dst < cols, elem_bytes not 1, 2 or 4 ->
+ * GPTQ_E_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+int gptq_gather(const void* src, int elem_bytes, int64_t src_rows, int64_t src_cols, int64_t ld_src,
+                const int32_t* row_idx, int64_t rows, const int32_t* col_idx, int64_t cols, void* dst,
+                int64_t ld_dst, int32_t* info, void* stream);
+
+/* ------------------------------------------------------------------------
  * Use of the packed layer: quantized matrix x full-precision vectors.
  *
  * Defines: xuzou.cn reading card of the GPTQ paper, section 方法适配 (last

@@ -40,6 +40,11 @@ _SIGNATURES = {
         [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr],
     ),
     "gptq_pack_codes": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr]),
+    "gptq_act_order_perm": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "gptq_gather": (
+        _c_int,
+        [_c_ptr, _c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr],
+    ),
     "gptq_dequant_matvec": (
         _c_int,
         [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr],
@@ -259,6 +264,55 @@ def gptq_pack_codes(codes: torch.Tensor, bits: int, packed: Optional[torch.Tenso
         packed = torch.empty((d_row, words_per_row(d_col, bits)), dtype=torch.int32, device=codes.device)
     _check("gptq_pack_codes", load().gptq_pack_codes(_ptr(codes), d_row, d_col, bits, _ptr(packed), _stream()))
     return packed
+
+
+# ------------------------------------------------------------ column order
+def gptq_act_order_perm(H: torch.Tensor, perm: Optional[torch.Tensor] = None,
+                        invperm: Optional[torch.Tensor] = None):
+    """(perm, invperm), int32 [d]: columns by descending diag(H) (ties by
+    index, NaN last); perm[q] is the original column taken q-th."""
+    _on_gpu("H", H)
+    if H.dtype != torch.float32 or H.dim() != 2 or H.shape[0] != H.shape[1] or H.stride(1) != 1:
+        raise ValueError("H must be a float32 [d, d] tensor with unit column stride")
+    d = H.shape[0]
+    if perm is None:
+        perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    if invperm is None:
+        invperm = torch.empty(d, dtype=torch.int32, device=H.device)
+    _check("gptq_act_order_perm", load().gptq_act_order_perm(_ptr(H), d, H.stride(0), _ptr(perm), _ptr(invperm),
+                                                             _stream()))
+    return perm, invperm
+
+
+def gptq_gather(src: torch.Tensor, row_idx: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, info: Optional[torch.Tensor] = None):
+    """out[i][q] = src[row_idx[i]][col_idx[q]] (identity where an index is
+    None) for 2-D src with 1-, 2- or 4-byte elements; returns (out, info),
+    info[0] = 1 if an index was out of range."""
+    _on_gpu("src", src)
+    if src.dim() != 2 or src.stride(1) != 1 or src.element_size() not in (1, 2, 4):
+        raise ValueError("src must be 2-D with unit column stride and 1-, 2- or 4-byte elements")
+    for name, t in (("row_idx", row_idx), ("col_idx", col_idx)):
+        if t is not None:
+            _on_gpu(name, t)
+            if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 vector")
+    rows = src.shape[0] if row_idx is None else row_idx.shape[0]
+    cols = src.shape[1] if col_idx is None else col_idx.shape[0]
+    if out is None:
+        out = torch.empty((rows, cols), dtype=src.dtype, device=src.device)
+    if out.shape != (rows, cols) or out.dtype != src.dtype or out.stride(1) != 1:
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if info is None:
+        info = torch.empty(1, dtype=torch.int32, device=src.device)
+    _check(
+        "gptq_gather",
+        load().gptq_gather(
+            _ptr(src), src.element_size(), src.shape[0], src.shape[1], max(src.stride(0), src.shape[1]),
+            _ptr(row_idx), rows, _ptr(col_idx), cols, _ptr(out), max(out.stride(0), cols), _ptr(info), _stream(),
+        ),
+    )
+    return out, info
 
 
 # ------------------------------------------------------------ packed use
