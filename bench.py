@@ -187,6 +187,61 @@ def matvec_measure(g, torch, q, W, cfg, reps=50, replays=10):
     }
 
 
+def act_order_measure(g, torch, H, W, q_nat, cfg, ws_u, ws_q, steps=3):
+    """The layer in act-order from the same Hessian: permutation, gathers of
+    H and W, factor, sweep, and the codes gathered back to the original
+    column order, each timed with HIP events on the current stream. Reports
+    the per-step time of these stages, the W gather's HBM rate, and the
+    layer loss beside the natural order's."""
+    dev = W.device
+    d = H.shape[0]
+    perm = torch.empty(d, dtype=torch.int32, device=dev)
+    inv = torch.empty(d, dtype=torch.int32, device=dev)
+    Hp = torch.empty_like(H)
+    Wp = torch.empty_like(W)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    hv = g.Hinv(torch.empty_like(H), torch.empty((), dtype=torch.float32, device=dev),
+                torch.empty((), dtype=torch.int32, device=dev))
+    q = g.gptq_quantize_layer(W, H, cfg.bits, cfg.group_size, cfg.block, ws=ws_q)  # allocates the outputs once
+    codes_orig = torch.empty_like(q.codes)
+    names = ["perm", "gather_H", "prepare_hinv", "gather_W", "quantize_layer", "gather_codes"]
+
+    def run(ev=None):
+        calls = [
+            lambda: g.gptq_act_order_perm(H, perm, inv),
+            lambda: g.gptq_gather(H, perm, perm, out=Hp, info=info),
+            lambda: g.gptq_prepare_hinv(Hp, cfg.damp, ws=ws_u, out=hv),
+            lambda: g.gptq_gather(W, None, perm, out=Wp, info=info),
+            lambda: g.gptq_quantize_layer(Wp, hv.U, cfg.bits, cfg.group_size, cfg.block, ws=ws_q, out=q),
+            lambda: g.gptq_gather(q.codes, None, inv, out=codes_orig, info=info),
+        ]
+        for k, c in enumerate(calls):
+            if ev:
+                ev[k].record()
+            c()
+        if ev:
+            ev[len(calls)].record()
+
+    run()
+    torch.cuda.synchronize()
+    if int(hv.info.item()) != 0 or int(info.item()) != 0:
+        raise RuntimeError("act-order path failed")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    for k in range(steps):
+        run(evs[k])
+    torch.cuda.synchronize()
+    t = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    w_bytes = 2.0 * W.numel() * W.element_size()
+    return {
+        "stages_ms": t,
+        "ms_after_hessian": float(sum(t.values())),
+        "gather_W_gbps": w_bytes / (t["gather_W"] * 1e-3) / 1e9,
+        "loss_act_order": float(q.loss.item()),
+        "loss_natural_order": float(q_nat.loss.item()),
+        "steps": steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +387,10 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    out["act_order"] = act_order_measure(g, torch, H, W, q, cfg, ws_u, ws_q)
+    ao = out["act_order"]
+    log(f"bench: act-order path after H {ao['ms_after_hessian']:.3f} ms {ao['stages_ms']}; "
+        f"loss {ao['loss_act_order']:.6g} (natural order {ao['loss_natural_order']:.6g})")
     out["dequant_matvec"] = matvec_measure(g, torch, q, W, cfg)
     log(f"bench: packed matrix-vector product {out['dequant_matvec']['us']:.2f} us "
         f"({out['dequant_matvec']['gbps']:.0f} GB/s); dense fp16 {out['dequant_matvec']['fp16_dense_us']:.2f} us")

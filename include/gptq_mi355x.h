@@ -168,7 +168,7 @@ int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col,
  *   H        device fp32, d x d, row stride ldh >= d; only the diagonal is read.
  *   perm     device int32 [d]: perm[q] = original column quantized q-th.
  *   invperm  device int32 [d]: invperm[perm[q]] = q (also the rank buffer).
- * Runs on `stream`; nothing is allocated. Errors: d < 1, d > 2^27, ldh < d,
+ * Runs on `stream`; nothing is allocated. Errors: d < 1, d > 65535 * 256, ldh < d,
  * NULL pointers -> GPTQ_E_INVALID_ARG.
  * ---------------------------------------------------------------------- */
 int gptq_act_order_perm(const float* H, int64_t d, int64_t ldh, int32_t* perm, int32_t* invperm,

@@ -17,7 +17,7 @@ namespace gptq {
 namespace {
 
 constexpr int RANK_THREADS = 256;
-constexpr int RANK_SLICE = 2048;  // diagonal entries per workgroup (8 KB of LDS)
+constexpr int RANK_SLICE = 256;  // diagonal entries per workgroup: d/256 x d/256 workgroups
 
 // Key of a total order in which a larger key comes first: NaN -> 0 (after
 // every number), -0 -> +0, otherwise the float's bits mapped monotonically
@@ -63,7 +63,8 @@ __global__ void act_order_scatter(const int32_t* __restrict__ rank, int64_t d, i
 // dst[i][q] = src[row_idx[i]][col_idx[q]] (identity where an index array is
 // NULL); an index outside the source writes 0 and sets *info = 1. One
 // workgroup per destination row (grid-stride over rows), threads along the
-// row: coalesced writes, reads gathered inside one source row.
+// row: coalesced writes, reads gathered inside one source row. Used for
+// source rows longer than the LDS staging buffer.
 template <typename T>
 __global__ void __launch_bounds__(256)
 gather_kernel(const T* __restrict__ src, int64_t src_rows, int64_t src_cols, int64_t lds,
@@ -83,13 +84,70 @@ gather_kernel(const T* __restrict__ src, int64_t src_rows, int64_t src_cols, int
   }
 }
 
+constexpr int GATHER_LDS_MAX = 65536;  // bytes of one staged source row
+
+// Same result as gather_kernel, for source rows of at most GATHER_LDS_MAX
+// bytes: the source row is first copied into LDS with coalesced loads (16
+// bytes per lane when VEC: every row 16-byte aligned), then gathered from
+// LDS. The dynamic LDS size is the row length rounded up to 16 bytes. The
+// row index, and so every branch around the barriers, is uniform across
+// the workgroup.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256)
+gather_lds_kernel(const T* __restrict__ src, int64_t src_rows, int64_t src_cols, int64_t lds,
+                  const int32_t* __restrict__ ridx, int64_t rows, const int32_t* __restrict__ cidx, int64_t cols,
+                  T* __restrict__ dst, int64_t ldd, int32_t* __restrict__ info) {
+  extern __shared__ uint4 stage4[];
+  T* stage = reinterpret_cast<T*>(stage4);
+  constexpr int V = 16 / sizeof(T);
+  const int nc = int(src_cols);
+  for (int64_t i = blockIdx.x; i < rows; i += gridDim.x) {
+    const int64_t si = ridx ? int64_t(ridx[i]) : i;
+    const bool rok = si >= 0 && si < src_rows;
+    if (rok) {
+      const T* srow = src + si * lds;
+      int t0 = 0;
+      if (VEC) {
+        const uint4* s4 = reinterpret_cast<const uint4*>(srow);
+        const int nv = nc / V;
+        for (int t = threadIdx.x; t < nv; t += blockDim.x) stage4[t] = s4[t];
+        t0 = nv * V;
+      }
+      for (int t = t0 + threadIdx.x; t < nc; t += blockDim.x) stage[t] = srow[t];
+    }
+    __syncthreads();
+    T* drow = dst + i * ldd;
+    for (int64_t q = threadIdx.x; q < cols; q += blockDim.x) {
+      const int64_t sq = cidx ? int64_t(cidx[q]) : q;
+      const bool ok = rok && sq >= 0 && sq < src_cols;
+      drow[q] = ok ? stage[sq] : T(0);
+      if (!ok && info) *info = 1;
+    }
+    __syncthreads();  // the next row overwrites the stage
+  }
+}
+
 template <typename T>
 int launch_gather(const void* src, int64_t src_rows, int64_t src_cols, int64_t lds, const int32_t* ridx,
                   int64_t rows, const int32_t* cidx, int64_t cols, void* dst, int64_t ldd, int32_t* info,
                   hipStream_t s) {
   const unsigned grid = unsigned(rows < 65536 ? rows : 65536);
-  hipLaunchKernelGGL((gather_kernel<T>), dim3(grid), dim3(256), 0, s, static_cast<const T*>(src), src_rows, src_cols,
-                     lds, ridx, rows, cidx, cols, static_cast<T*>(dst), ldd, info);
+  const T* sp = static_cast<const T*>(src);
+  T* dp = static_cast<T*>(dst);
+  const int64_t row_bytes = src_cols * int64_t(sizeof(T));
+  if (row_bytes <= GATHER_LDS_MAX) {
+    const size_t smem = align_up(size_t(row_bytes), 16);
+    const bool vec = reinterpret_cast<uintptr_t>(src) % 16 == 0 && (lds * int64_t(sizeof(T))) % 16 == 0;
+    if (vec)
+      hipLaunchKernelGGL((gather_lds_kernel<T, true>), dim3(grid), dim3(256), smem, s, sp, src_rows, src_cols, lds,
+                         ridx, rows, cidx, cols, dp, ldd, info);
+    else
+      hipLaunchKernelGGL((gather_lds_kernel<T, false>), dim3(grid), dim3(256), smem, s, sp, src_rows, src_cols, lds,
+                         ridx, rows, cidx, cols, dp, ldd, info);
+  } else {
+    hipLaunchKernelGGL((gather_kernel<T>), dim3(grid), dim3(256), 0, s, sp, src_rows, src_cols, lds, ridx, rows, cidx,
+                       cols, dp, ldd, info);
+  }
   return launch_status();
 }
 
@@ -100,7 +158,7 @@ using namespace gptq;
 
 extern "C" int gptq_act_order_perm(const float* H, int64_t d, int64_t ldh, int32_t* perm, int32_t* invperm,
                                    void* stream) {
-  if (d < 1 || d > (int64_t(1) << 27) || ldh < d || !H || !perm || !invperm) return GPTQ_E_INVALID_ARG;
+  if (d < 1 || d > int64_t(65535) * RANK_SLICE || ldh < d || !H || !perm || !invperm) return GPTQ_E_INVALID_ARG;
   hipStream_t s = as_stream(stream);
   const unsigned fb = unsigned(d / 256 + 1 < 4096 ? d / 256 + 1 : 4096);
   hipLaunchKernelGGL(fill_i32, dim3(fb), dim3(256), 0, s, invperm, d, 0);

@@ -61,6 +61,30 @@ def test_gather_parity(gpu, dtype, use_rows, use_cols):
     assert int(info.item()) == 0
 
 
+@pytest.mark.parametrize("dtype,cols,ld", [
+    (torch.float16, 777, 781),     # staged in LDS, rows not 16-byte aligned (element loads)
+    (torch.uint8, 1000, 1003),     # the same for bytes
+    (torch.float32, 20000, 20000), # 80 KB rows: gathered straight from global memory
+    (torch.float16, 32768, 32768), # exactly 64 KB rows: the largest staged row
+])
+def test_gather_parity_row_layouts(gpu, dtype, cols, ld):
+    r = np.random.default_rng(cols)
+    rows = 9
+    npdt = {torch.float16: np.float16, torch.float32: np.float32, torch.uint8: np.uint8}[dtype]
+    src_np = (r.integers(0, 255, size=(rows, cols)) if dtype == torch.uint8 else r.standard_normal((rows, cols)))
+    src_np = src_np.astype(npdt)
+    buf = torch.zeros((rows, ld), dtype=dtype, device=DEV)
+    buf[:, :cols] = gpu_tensor(src_np)
+    src = buf[:, :cols]
+    ri = r.permutation(rows).astype(np.int32)
+    ci = r.integers(0, cols, size=cols + 5).astype(np.int32)
+    out, info = gpu.gptq_gather(src, gpu_tensor(ri), gpu_tensor(ci))
+    torch.cuda.synchronize()
+    ref = np.ascontiguousarray(src_np[ri][:, ci])
+    assert np.array_equal(out.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+    assert int(info.item()) == 0
+
+
 def test_gather_reports_bad_indices(gpu):
     src = torch.arange(1, 1 + 6 * 10, dtype=torch.float32, device=DEV).reshape(6, 10)
     ri = torch.tensor([0, 5, 6, -1], dtype=torch.int32, device=DEV)

@@ -32,7 +32,7 @@ FULL_SIZE = [
 ]
 N_SAMPLE_ROWS = 256
 
-# Per activation recipe and damping: the oracle's U in fp32.
+# Per activation recipe and damping: the oracle's H and U in fp32.
 _cache = {}
 
 
@@ -83,10 +83,16 @@ def factor_stage(gpu, cfg, Hf):
 
 
 def prepared(gpu, cfg):
+    """The oracle's factor in fp32 (after the Hessian and factor stages ran
+    once for this activation recipe)."""
+    return _prepared(gpu, cfg)[1]
+
+
+def _prepared(gpu, cfg):
     key = x_key(cfg) + (cfg.damp,)
     if key not in _cache:
         Hf = hessian_stage(gpu, cfg)
-        _cache[key] = factor_stage(gpu, cfg, Hf)
+        _cache[key] = (Hf.astype(np.float32), factor_stage(gpu, cfg, Hf))
     return _cache[key]
 
 
@@ -109,3 +115,36 @@ def test_full_size_layer(gpu, name):
     zeros = q.zeros.cpu().numpy()
     assert zeros.min() >= 0 and zeros.max() <= (1 << cfg.bits) - 1
     assert bool(torch.all(q.scales > 0)) and bool(torch.isfinite(q.loss))
+
+
+@pytest.mark.timeout(900)
+def test_full_size_act_order_layer(gpu):
+    """The 4096x4096 3-bit g128 layer in act-order, in the launch
+    configuration the benchmark times: permutation (bit-exact), gathers,
+    factor and sweep on the GPU; the oracle's act-order layer on 256 sampled
+    rows from the same fp32 Hessian."""
+    cfg = CONFIGS["attn_proj_4096x4096_3bit_g128"]
+    say(f"full-size act-order {cfg.name}")
+    H32, _ = _prepared(gpu, cfg)
+    W = weights(cfg)
+    Hg = gpu_tensor(H32)
+    perm, inv = gpu.gptq_act_order_perm(Hg)
+    Hp, i1 = gpu.gptq_gather(Hg, perm, perm)
+    hv = gpu.gptq_prepare_hinv(Hp, cfg.damp)
+    Wp, i2 = gpu.gptq_gather(gpu_tensor(W), None, perm)
+    q = gpu.gptq_quantize_layer(Wp, hv.U, cfg.bits, cfg.group_size, cfg.block)
+    torch.cuda.synchronize()
+    assert int(hv.info.item()) == 0 and int(i1.item()) == 0 and int(i2.item()) == 0
+    p = O.act_order_perm(H32.astype(np.float64))
+    assert np.array_equal(perm.cpu().numpy(), p)
+    U_ref, _ = O.prepare_hinv(H32.astype(np.float64)[np.ix_(p, p)], cfg.damp)
+    e = rel_fro(hv.U.cpu().numpy(), U_ref)
+    say(f"act-order U rel fro {e:.3g}")
+    assert e < 1e-6
+    rows = np.sort(np.random.default_rng(8).choice(cfg.d_row, N_SAMPLE_ROWS, replace=False))
+    rows[-1] = cfg.d_row - 1
+    rows = np.unique(rows)
+    ref = O.quantize_layer(W[rows][:, p], U_ref.astype(np.float32).astype(np.float64), cfg.bits, cfg.group_size,
+                           cfg.block, decide=np.float32)
+    m = check_quant(q, ref, cfg.bits, rows=rows)
+    say(f"act-order sampled rows {len(rows)}, codes match {m:.6f}")
