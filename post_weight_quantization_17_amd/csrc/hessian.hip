@@ -247,16 +247,8 @@ __device__ __forceinline__ half8 tr_frag(const unsigned char* lds, int off) {
 }
 
 // Interior tiles (both panels inside the matrix), whole 128-token blocks of
-// 4 steps. Four LDS stages: step s + 3 is loaded while step s is computed.
-//
-// Software pipeline per step s (buffer s % 4):
-//   barrier (all loads issued so far have landed)
-//   MFMAs of the first 16 tokens (fragments already in registers)
-//     ... meanwhile: issue the loads of step s + 3, read the fragments of the
-//         last 16 tokens
-//   MFMAs of the last 16 tokens
-//     ... meanwhile: read the first-16-token fragments of step s + 1
-// so the MFMA pipe has queued work right after every barrier.
+// 4 steps. Four LDS stages: stage s + 3 is loaded while stage s is computed;
+// the schedule of one step is described at its definition below.
 constexpr int S_NSTAGE = 4;
 
 // Work order (XCD aware). Workgroups are dispatched round-robin over the 8
@@ -356,32 +348,56 @@ syrk_f16_lds(const __half* __restrict__ X, int64_t n_main, int64_t ldx, int nb, 
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   };
-  // Stages s and s + 1 complete plus barrier. __syncthreads() carries a
-  // release fence, which also waits for the loads already issued for later
-  // stages; a bare s_barrier after a counted vmcnt wait would let up to two
-  // stages stay in flight, but measured slower on this kernel (5.17 vs
-  // 4.93 ms at 262144 x 4096): draining at every step keeps the workgroups
-  // in step with each other, so they share the same token slices in cache
-  // and the loads do not land in LDS while the fragments are read.
-  auto wait2 = [&](int) { __syncthreads(); };
-  // sched_barrier(0) between phases keeps the scheduler from hoisting later
-  // reads (which would only add live registers).
+  // One step s (32 tokens) in two MFMA groups of 16, with the LDS reads and
+  // the direct loads placed between the MFMAs (one wave per SIMD, so a read
+  // issued after a group would leave the matrix pipe idle while it lands):
+  //   group A: MFMAs on stage s, tokens 0-15 (fa0/fb0), interleaved with the
+  //            loads of stage s + 3 and the reads of stage s, tokens 16-31
+  //   wait:    own loads of stage s + 1 landed (stages s + 2 and s + 3 stay in
+  //            flight: vmcnt 16), own LDS reads done; barrier
+  //   group B: MFMAs on stage s, tokens 16-31 (fa1/fb1), interleaved with the
+  //            reads of stage s + 1, tokens 0-15
+  // The barrier of step s orders every hand-off: stage s + 1 has landed for
+  // all waves before group B reads it, and every wave has finished reading
+  // stage s - 1 (groups A and B of earlier steps) before group A of step s
+  // loads stage s + 3 into that buffer. Loads past the last step re-load the
+  // last step (valid memory, never read), so the load count per step, and
+  // with it the vmcnt of the wait, is constant.
   auto step = [&](int s, unsigned char* cur, unsigned char* next, unsigned char* later) {
-    wait2(s);
-    mfma16(fa0, fb0);
-    if (s + 3 < nsteps) issue(s + 3, later);
+    issue(s + 3 < nsteps ? s + 3 : nsteps - 1, later);
     read_frags(cur, 1, fa1, fb1);
+    mfma16(fa0, fb0);
+    // Reads and loads go with the first 8 MFMAs, so they land while the
+    // last 8 run.
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x4070);  // vmcnt(16) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(next, 0, fa0, fb0);
     mfma16(fa1, fb1);
-    if (s + 1 < nsteps) read_frags(next, 0, fa0, fb0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
 
   if (nsteps > 0) {
     issue(0, lds0);
-    issue(1, lds1);
-    issue(2, lds2);
-    __syncthreads();
+    issue(1 < nsteps ? 1 : nsteps - 1, lds1);
+    issue(2 < nsteps ? 2 : nsteps - 1, lds2);
+    __builtin_amdgcn_s_waitcnt(0x4070);  // stage 0 landed (vmcnt 16)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     read_frags(lds0, 0, fa0, fb0);
   }
   for (int s = 0; s < nsteps; s += S_NSTAGE) {
@@ -390,6 +406,7 @@ syrk_f16_lds(const __half* __restrict__ X, int64_t n_main, int64_t ldx, int nb, 
     step(s + 2, lds2, lds3, lds1);
     step(s + 3, lds3, lds0, lds2);
   }
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no direct load outlives the workgroup's LDS
 
   // Partial tile, row-major [256][256]. 32x32 MFMA result layout: lane l holds
   // column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for register r.
@@ -535,6 +552,25 @@ SyrkPlan plan_syrk(int64_t n_tokens, int64_t d, int xdtype) {
   const int64_t ksteps = (p.n_full + unit - 1) / unit;
   int64_t want = (2048 + p.ntiles - 1) / p.ntiles;
   if (want < 4) want = 4;
+  if (f16) {
+    // One workgroup per CU at a time: among 4 .. 2 want splits, take the
+    // count whose last round of 256 workgroups is fullest (ties: fewer
+    // splits, i.e. fewer partial tiles to reduce).
+    const int64_t tiles = int64_t(d / p.T) * (d / p.T + 1) / 2;
+    if (tiles > 0) {
+      double best = -1.0;
+      int64_t pick = want;
+      for (int64_t n = 4; n <= 2 * want; ++n) {
+        const double rounds = double(tiles * n) / 256.0;
+        const double eff = rounds / double(int64_t(rounds) + (rounds > double(int64_t(rounds)) ? 1 : 0));
+        if (eff > best + 0.005) {
+          best = eff;
+          pick = n;
+        }
+      }
+      want = pick;
+    }
+  }
   if (want > ksteps) want = ksteps;
   if (want < 1) want = 1;
   p.tokens_per_split = ((ksteps + want - 1) / want) * unit;
