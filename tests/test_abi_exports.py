@@ -59,8 +59,11 @@ def test_workspace_sizes(lib):
     for f in ("gptq_hessian_workspace_size", "gptq_prepare_hinv_workspace_size", "gptq_quantize_layer_workspace_size"):
         getattr(lib, f).restype = ctypes.c_size_t
     i64 = ctypes.c_int64
-    # Hessian: 16 splits x 136 upper 256-tiles x 256 KB at the 4096-wide, 262144-token layer
-    assert lib.gptq_hessian_workspace_size(i64(262144), i64(4096), 0) == 16 * 136 * 256 * 256 * 4
+    # Hessian: 15 token splits x 136 upper 256-tiles x 256 KB at the 4096-wide, 262144-token layer
+    # (15 x 136 = 2040 workgroups fill 7.97 rounds of 256 one-per-CU slots; 16 would leave half a round)
+    assert lib.gptq_hessian_workspace_size(i64(262144), i64(4096), 0) == 15 * 136 * 256 * 256 * 4
+    # 12288 wide: 5 splits x 1176 tiles (5880 workgroups, 22.97 rounds)
+    assert lib.gptq_hessian_workspace_size(i64(262144), i64(12288), 0) == 5 * 1176 * 256 * 256 * 4
     assert lib.gptq_hessian_workspace_size(i64(10), i64(0), 0) == 0
     assert lib.gptq_hessian_workspace_size(i64(10), i64(8), 7) == 0
     # inverse factor: two fp64 d x d matrices plus small scalars
