@@ -155,6 +155,25 @@ int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col,
                         double* loss, float* row_loss, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Dequantize the packed layer (for running the quantized layer, e.g. to
+ * propagate calibration activations to the next layer).
+ *
+ * Defines: astro-blog survey, section 1.2 (dequantization s (x_q - z));
+ * xuzou.cn reading card, section 计算设置 (the quantized block is run to
+ * produce the next block's inputs).
+ *   out[r][c] = s[r][g(c)] * (code[r][c] - zeros[r][g(c)]), the product in
+ *   fp32, then rounded to nearest even in the output type.
+ *   packed, scales, zeros   as for gptq_quantize_layer.
+ *   group_size -1 or >= 1; out_dtype GPTQ_F16 or GPTQ_F32; out device,
+ *   d_row x d_col, row stride ld_out >= d_col.
+ * Runs on `stream`; nothing is allocated. Errors: sizes < 1, NULL pointers,
+ * ld_out < d_col, bad bits, group or dtype -> GPTQ_E_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+int gptq_dequantize(const uint32_t* packed, const float* scales, const int32_t* zeros, int64_t d_row,
+                    int64_t d_col, int bits, int64_t group_size, void* out, int out_dtype, int64_t ld_out,
+                    void* stream);
+
+/* ------------------------------------------------------------------------
  * Column order: act-order permutation.
  *
  * Defines: mcipr.com "一文读懂GPTQ", section 四 (the desc_act flag of the

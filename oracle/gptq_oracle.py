@@ -61,6 +61,16 @@ the design notes of the repository):
   reference: per row, repeatedly the free weight with the least
   (w - quant(w))^2 / [H_F^-1]_qq, with the inverse of the free sub-Hessian
   kept by Gaussian elimination; one grid per row from the original row.
+* Calibration pipeline (xuzou.cn reading card, section 计算设置: one
+  block at a time, the quantized block's outputs are the next block's
+  inputs). Layers reading the same input (the q/k/v projections) share
+  one Hessian, accumulated over the calibration chunks, and one factor.
+  Inside a block each layer's Hessian comes from its input as produced by
+  the already-quantized layers before it. The MLP block is
+  X1 = relu(X0 What_up^T), X2 = X1 What_down^T (ReLU: the OPT models the
+  pages quantize); the layer weights used to run the block are the
+  dequantized weights held as fp16 (s (code - z) in fp32, rounded to
+  fp16), and the activations between layers are stored as fp16.
 * Packing: per row, an LSB-first bitstream along the columns; code j fills
   bits [b j, b j + b) and word k holds bits [32 k, 32 k + 32); rows are
   zero-padded to ceil(d_col b / 32) words.
@@ -474,6 +484,64 @@ def obq_greedy(W: np.ndarray, H: np.ndarray, bits: int, damp: float = 0.01, deci
             Wq[r, q] = what
             taken[r, step] = q
     return dict(codes=codes, Wq=Wq, row_loss=row_loss, loss=float(np.sum(row_loss)), order=taken)
+
+
+# --------------------------------------------------------------------------
+# Calibration pipeline: layers sharing an input, and a block quantized
+# layer by layer with the quantized layers' outputs as the next inputs
+# --------------------------------------------------------------------------
+def quantize_shared_input(chunks, Ws, bits: int, group_size: int, block: int = 128, damp: float = 0.01,
+                          decide=F64, symmetric: bool = False):
+    """Layers that read the same input (xuzou.cn reading card, section
+    计算设置; the q/k/v projections of a block): one Hessian summed over the
+    calibration chunks, one damped factor, and each layer's rows swept with
+    it (section 方法适配: every row uses the same inverse-Hessian
+    information). Returns dict(H, U, lam, layers=[quantize_layer dict per W]).
+    """
+    H = hessian(chunks)
+    U, lam = prepare_hinv(H, damp)
+    layers = [quantize_layer(W, U, bits, group_size, block, decide, symmetric) for W in Ws]
+    return dict(H=H, U=U, lam=lam, layers=layers)
+
+
+def model_weight_f16(codes, scales, zeros, group_size: int) -> np.ndarray:
+    """The dequantized weights as the layer holds them to run: s (code - z)
+    with the product rounded to float32, then to float16 (astro-blog
+    survey, section 1.2)."""
+    codes = np.asarray(codes)
+    d_col = codes.shape[1]
+    gi = np.zeros(d_col, dtype=np.int64) if group_size == -1 else np.arange(d_col) // group_size
+    s32 = np.asarray(scales, np.float32)[:, gi]
+    k32 = (codes.astype(np.int64) - np.asarray(zeros, np.int64)[:, gi]).astype(np.float32)
+    return (s32 * k32).astype(np.float16)
+
+
+def quantize_mlp_block(X0, W_up, W_down, bits: int, group_size: int, block: int = 128, damp: float = 0.01,
+                       decide=F64):
+    """One MLP block quantized layer by layer (xuzou.cn reading card,
+    section 计算设置): H_up from the block input X0 [tokens, d_model];
+    quantize W_up [d_ff, d_model]; run the quantized up layer,
+    X1 = fp16(relu(X0 What_up^T)) with What_up the fp16 model weight and the
+    product exact; H_down from X1; quantize W_down [d_model, d_ff]; the block
+    output X2 = fp16(X1 What_down^T) is the next block's input.
+    Returns dict(up, down (quantize_layer dicts plus H, U, lam), X1, X2).
+    """
+    X0 = np.asarray(X0)
+    out = {}
+    H_up = hessian(X0)
+    U_up, lam_up = prepare_hinv(H_up, damp)
+    up = quantize_layer(W_up, U_up, bits, group_size, block, decide)
+    up.update(H=H_up, U=U_up, lam=lam_up)
+    Wh_up = model_weight_f16(up["codes"], up["scales"], up["zeros"], group_size)
+    X1 = np.maximum(X0.astype(F64) @ Wh_up.astype(F64).T, 0.0).astype(np.float16)
+    H_down = hessian(X1)
+    U_down, lam_down = prepare_hinv(H_down, damp)
+    down = quantize_layer(W_down, U_down, bits, group_size, block, decide)
+    down.update(H=H_down, U=U_down, lam=lam_down)
+    Wh_down = model_weight_f16(down["codes"], down["scales"], down["zeros"], group_size)
+    X2 = (X1.astype(F64) @ Wh_down.astype(F64).T).astype(np.float16)
+    out.update(up=up, down=down, X1=X1, X2=X2)
+    return out
 
 
 def layer_loss_direct(X: np.ndarray, W: np.ndarray, Wq: np.ndarray, lam: float = 0.0) -> float:

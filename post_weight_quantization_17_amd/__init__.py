@@ -40,6 +40,7 @@ _SIGNATURES = {
         [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr],
     ),
     "gptq_pack_codes": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr]),
+    "gptq_dequantize": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_int, _c_i64, _c_ptr]),
     "gptq_act_order_perm": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "gptq_gather": (
         _c_int,
@@ -264,6 +265,34 @@ def gptq_pack_codes(codes: torch.Tensor, bits: int, packed: Optional[torch.Tenso
         packed = torch.empty((d_row, words_per_row(d_col, bits)), dtype=torch.int32, device=codes.device)
     _check("gptq_pack_codes", load().gptq_pack_codes(_ptr(codes), d_row, d_col, bits, _ptr(packed), _stream()))
     return packed
+
+
+def gptq_dequantize(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, d_col: int, bits: int,
+                    group_size: int, dtype: torch.dtype = torch.float16,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """What [d_row, d_col] = s (code - z), computed in fp32 and rounded to
+    ``dtype`` (float16 or float32)."""
+    for name, t in (("packed", packed), ("scales", scales), ("zeros", zeros)):
+        _on_gpu(name, t)
+    d_row = packed.shape[0]
+    if (packed.dim() != 2 or packed.shape[1] != words_per_row(d_col, bits) or not packed.is_contiguous()
+            or packed.dtype not in (torch.int32, torch.uint32)):
+        raise ValueError("packed must be a contiguous [d_row, words_per_row] 32-bit tensor")
+    ng = n_groups(d_col, group_size) if group_size == -1 or group_size > 0 else 1
+    if scales.shape != (d_row, ng) or scales.dtype != torch.float32 or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous float32 [d_row, n_groups] tensor")
+    if zeros.shape != (d_row, ng) or zeros.dtype != torch.int32 or not zeros.is_contiguous():
+        raise ValueError("zeros must be a contiguous int32 [d_row, n_groups] tensor")
+    if out is None:
+        out = torch.empty((d_row, d_col), dtype=dtype, device=packed.device)
+    if out.shape != (d_row, d_col) or out.stride(1) != 1 or out.dtype not in (torch.float16, torch.float32):
+        raise ValueError("out must be float16/float32 [d_row, d_col] with unit column stride")
+    _check(
+        "gptq_dequantize",
+        load().gptq_dequantize(_ptr(packed), _ptr(scales), _ptr(zeros), d_row, d_col, bits, group_size, _ptr(out),
+                               _dtype_code(out), max(out.stride(0), d_col), _stream()),
+    )
+    return out
 
 
 # ------------------------------------------------------------ column order

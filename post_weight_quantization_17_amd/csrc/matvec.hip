@@ -533,6 +533,43 @@ int launch_bits(bool pairs, int nb, bool vecx, const uint32_t* packed, const flo
   return launch_nb<BITS, 1>(vecx, packed, scales, zeros, d_row, d_col, nwords, group, ngroups, x, ldx, y, ldy, s);
 }
 
+// What[r][c] = fp(s[r][g(c)] * (code[r][c] - z[r][g(c)])): the product in
+// fp32 (code - z is an exact small integer), then rounded to the output type
+// (round to nearest even). One workgroup per row (grid-stride over rows),
+// threads along the row; every code is cut from at most two words of the
+// row's stream, inside the row's words.
+template <typename OT>
+__global__ void __launch_bounds__(256)
+dequantize_kernel(const uint32_t* __restrict__ packed, const float* __restrict__ scales,
+                  const int32_t* __restrict__ zeros, int d_row, int d_col, int nwords, int bits, int group,
+                  int ngroups, OT* __restrict__ out, int64_t ldo) {
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t r = blockIdx.x; r < d_row; r += gridDim.x) {
+    const uint32_t* pr = packed + r * nwords;
+    const float* sr = scales + r * ngroups;
+    const int32_t* zr = zeros + r * ngroups;
+    OT* orow = out + r * ldo;
+    for (int c = threadIdx.x; c < d_col; c += blockDim.x) {
+      const int64_t bit = int64_t(c) * bits;
+      const int w = int(bit >> 5), off = int(bit & 31);
+      uint32_t v = pr[w] >> off;
+      if (off + bits > 32) v |= pr[w + 1] << (32 - off);  // word w + 1 holds the code's last bit: w + 1 < nwords
+      v &= mask;
+      const int g = group > 0 ? c / group : 0;
+      float val = sr[g] * (float(v) - float(zr[g]));
+      if constexpr (sizeof(OT) == 2) {
+        // Keep the fp32 product a value of its own: fused into one
+        // mixed-precision FMA with a +0 addend, the product would be rounded
+        // once to fp16 and a -0 product would come out as +0.
+        asm volatile("" : "+v"(val));
+        orow[c] = __float2half_rn(val);
+      } else {
+        orow[c] = val;
+      }
+    }
+  }
+}
+
 }  // namespace
 }  // namespace gptq
 
@@ -580,4 +617,26 @@ extern "C" int gptq_dequant_matvec(const uint32_t* packed, const float* scales, 
     b0 += nb;
   }
   return GPTQ_OK;
+}
+
+extern "C" int gptq_dequantize(const uint32_t* packed, const float* scales, const int32_t* zeros, int64_t d_row,
+                               int64_t d_col, int bits, int64_t group_size, void* out, int out_dtype, int64_t ld_out,
+                               void* stream) {
+  if (d_row < 1 || d_col < 1 || d_row > (int64_t(1) << 30) || d_col > (1 << 24)) return GPTQ_E_INVALID_ARG;
+  if (!packed || !scales || !zeros || !out || ld_out < d_col) return GPTQ_E_INVALID_ARG;
+  if (bits != 2 && bits != 3 && bits != 4 && bits != 8) return GPTQ_E_INVALID_ARG;
+  if (group_size != -1 && group_size < 1) return GPTQ_E_INVALID_ARG;
+  if (out_dtype != GPTQ_F16 && out_dtype != GPTQ_F32) return GPTQ_E_INVALID_ARG;
+  const int nwords = int((d_col * bits + 31) / 32);
+  const int ngroups = group_size == -1 ? 1 : int((d_col + group_size - 1) / group_size);
+  const int grp = group_size == -1 ? 0 : int(group_size);
+  const unsigned grid = unsigned(d_row < 65536 ? d_row : 65536);
+  hipStream_t s = as_stream(stream);
+  if (out_dtype == GPTQ_F16)
+    hipLaunchKernelGGL(dequantize_kernel<__half>, dim3(grid), dim3(256), 0, s, packed, scales, zeros, int(d_row),
+                       int(d_col), nwords, bits, grp, ngroups, static_cast<__half*>(out), ld_out);
+  else
+    hipLaunchKernelGGL(dequantize_kernel<float>, dim3(grid), dim3(256), 0, s, packed, scales, zeros, int(d_row),
+                       int(d_col), nwords, bits, grp, ngroups, static_cast<float*>(out), ld_out);
+  return launch_status();
 }

@@ -1,0 +1,164 @@
+"""Parity of the calibration pipeline (layers sharing an input, an MLP block
+quantized layer by layer) and of the dequantization, with the oracle (needs
+an MI355X).
+
+* gptq_dequantize: bit-exact against the float32 product rounded to the
+  output type.
+* Shared input: the stacked sweep is bit-exact against one sweep per layer
+  with the same factor (rows are independent); each layer against the
+  oracle as the plain sweep is compared.
+* MLP block: the up layer as the plain sweep. The activations X1 pass
+  through an fp16 GEMM (fp32 accumulation, rounded to fp16) on the GPU and an
+  exact product rounded to fp16 in the oracle, so some differ by one fp16
+  step (X1 within 2^-9 relative Frobenius), and H_down differs by rounding
+  (within 1e-3). The down layer is then checked twice: from the oracle's
+  own X1 (uploaded; oracle to GPU only), as strictly as the plain sweep; and
+  end to end, where a decision near a tie in H_down's last bits flips and the
+  rest of that row continues from it, so codes match on >= 95% of entries
+  and the loss within 2%.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gptq_oracle as O
+import post_weight_quantization_17_amd.pipeline as P
+from tests.test_gpu_parity import DEV, check_quant, gpu_tensor, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("d_row,d_col,bits,group,dtype", [
+    (1, 1, 4, -1, torch.float16),
+    (7, 33, 3, 16, torch.float32),
+    (5, 31, 2, 8, torch.float16),
+    (64, 256, 4, 128, torch.float16),
+    (100, 1000, 3, 40, torch.float32),
+    (33, 4096, 8, 128, torch.float16),
+])
+def test_dequantize_parity(gpu, d_row, d_col, bits, group, dtype):
+    r = np.random.default_rng(d_row + d_col)
+    codes = r.integers(0, 2**bits, size=(d_row, d_col))
+    ng = 1 if group == -1 else -(-d_col // group)
+    scales = r.uniform(-0.05, 0.05, size=(d_row, ng)).astype(np.float32)
+    zeros = r.integers(0, 2**bits, size=(d_row, ng)).astype(np.int32)
+    packed = O.pack(codes, bits)
+    out = gpu.gptq_dequantize(gpu_tensor(packed.view(np.int32)), gpu_tensor(scales), gpu_tensor(zeros), d_col, bits,
+                              group, dtype)
+    torch.cuda.synchronize()
+    gi = np.zeros(d_col, np.int64) if group == -1 else np.arange(d_col) // group
+    ref32 = scales[:, gi] * (codes - zeros[:, gi]).astype(np.float32)
+    ref = ref32.astype(np.float16) if dtype == torch.float16 else ref32
+    assert np.array_equal(out.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+    if dtype == torch.float16:
+        assert np.array_equal(out.cpu().numpy(), O.model_weight_f16(codes, scales, zeros, group))
+
+
+def test_dequantize_strided_output_and_bad_arguments(gpu):
+    r = np.random.default_rng(3)
+    codes = r.integers(0, 16, size=(9, 70))
+    scales = r.uniform(0.01, 0.02, size=(9, 1)).astype(np.float32)
+    zeros = r.integers(0, 16, size=(9, 1)).astype(np.int32)
+    buf = torch.full((9, 80), -7.0, dtype=torch.float32, device=DEV)
+    gpu.gptq_dequantize(gpu_tensor(O.pack(codes, 4).view(np.int32)), gpu_tensor(scales), gpu_tensor(zeros), 70, 4,
+                        -1, out=buf[:, :70])
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:, :70], scales * (codes - zeros).astype(np.float32))
+    assert np.all(got[:, 70:] == -7.0)  # untouched past d_col
+    lib = gpu.load()
+    p = buf.data_ptr()
+    E = gpu.GPTQ_E_INVALID_ARG
+    assert lib.gptq_dequantize(p, p, p, 4, 16, 5, -1, p, gpu.GPTQ_F32, 16, None) == E  # bits
+    assert lib.gptq_dequantize(p, p, p, 4, 16, 4, 0, p, gpu.GPTQ_F32, 16, None) == E  # group
+    assert lib.gptq_dequantize(p, p, p, 4, 16, 4, -1, p, 7, 16, None) == E  # dtype
+    assert lib.gptq_dequantize(p, p, p, 4, 16, 4, -1, p, gpu.GPTQ_F32, 15, None) == E  # ld_out
+
+
+def shared_inputs(seed, n, d, rows):
+    r = np.random.default_rng(seed)
+    X = r.standard_normal((n, d)).astype(np.float32)
+    X[:, r.choice(d, max(1, d // 100), replace=False)] *= 20.0
+    X *= r.lognormal(0.0, 0.5, size=(n, 1)).astype(np.float32)
+    X = X.astype(np.float16)
+    Ws = [(0.02 * r.standard_normal((k, d))).astype(np.float16) for k in rows]
+    return X, Ws
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (3, -1)])
+def test_shared_input_group(gpu, bits, group):
+    """q/k/v: one Hessian over three calibration chunks, one factor, one
+    stacked sweep."""
+    d, rows = 640, (96, 96, 160)
+    X, Ws = shared_inputs(11 + bits, 6000, d, rows)
+    cuts = [0, 2000, 4100, 6000]
+    chunks = [gpu_tensor(X[a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
+    H, hv, q, layers = P.quantize_shared_input(chunks, [gpu_tensor(W) for W in Ws], bits, group)
+    torch.cuda.synchronize()
+    ref = O.quantize_shared_input([X[a:b] for a, b in zip(cuts[:-1], cuts[1:])], Ws, bits, group, damp=0.01,
+                                  decide=np.float32)
+    e = rel_fro(H.cpu().numpy(), ref["H"])
+    say(f"shared input: H rel fro {e:.3g}")
+    assert e < 1e-4
+    for k, (W, lay) in enumerate(zip(Ws, layers)):
+        one = gpu.gptq_quantize_layer(gpu_tensor(W), hv.U, bits, group, 128)
+        torch.cuda.synchronize()
+        for name in ("codes", "scales", "zeros", "packed", "row_loss"):
+            assert torch.equal(getattr(lay, name), getattr(one, name)), (k, name)
+    # against the oracle, from the oracle's own factor (the GPU factor differs by rounding only)
+    for W, lay in zip(Ws, layers):
+        qk = gpu.gptq_quantize_layer(gpu_tensor(W), gpu_tensor(ref["U"].astype(np.float32)), bits, group, 128)
+        torch.cuda.synchronize()
+        check_quant(qk, O.quantize_layer(W, ref["U"].astype(np.float32).astype(np.float64), bits, group, 128,
+                                         decide=np.float32), bits)
+
+
+def test_mlp_block_pipeline(gpu):
+    """Up layer, ReLU, down layer, quantized in order on the GPU and by the
+    oracle from the same inputs."""
+    n, d_model, d_ff, bits, group = 4096, 512, 1376, 4, 128
+    r = np.random.default_rng(31)
+    X0 = r.standard_normal((n, d_model)).astype(np.float32)
+    X0[:, r.choice(d_model, 5, replace=False)] *= 10.0
+    X0 = X0.astype(np.float16)
+    W_up = (0.05 * r.standard_normal((d_ff, d_model))).astype(np.float16)
+    W_down = (0.05 * r.standard_normal((d_model, d_ff))).astype(np.float16)
+    b = P.quantize_mlp_block(gpu_tensor(X0), gpu_tensor(W_up), gpu_tensor(W_down), bits, group)
+    torch.cuda.synchronize()
+    ref = O.quantize_mlp_block(X0, W_up, W_down, bits, group, 128, 0.01, decide=np.float32)
+    assert rel_fro(b["H_up"].cpu().numpy(), ref["up"]["H"]) < 1e-4
+    assert int(b["hinv_up"].info.item()) == 0 and int(b["hinv_down"].info.item()) == 0
+    # the up layer from the GPU's own factor: near-tie flips only
+    check_quant(b["up"], ref["up"], bits)
+    ex1 = rel_fro(b["X1"].cpu().numpy(), ref["X1"])
+    eh = rel_fro(b["H_down"].cpu().numpy(), ref["down"]["H"])
+    say(f"mlp block: X1 rel fro {ex1:.3g}, H_down rel fro {eh:.3g}")
+    assert ex1 < 2.0**-9 and eh < 1e-3
+    # the down layer from the oracle's activations: as strict as the plain chain
+    X1r = gpu_tensor(ref["X1"])
+    Hd = gpu.gptq_hessian_accumulate(X1r)
+    hvd = gpu.gptq_prepare_hinv(Hd, 0.01)
+    qd = gpu.gptq_quantize_layer(gpu_tensor(W_down), hvd.U, bits, group, 128)
+    torch.cuda.synchronize()
+    assert rel_fro(Hd.cpu().numpy(), ref["down"]["H"]) < 1e-4 and int(hvd.info.item()) == 0
+    check_quant(qd, ref["down"], bits)
+    # end to end
+    codes = b["down"].codes.cpu().numpy().astype(np.int64)
+    rc = ref["down"]["codes"].astype(np.int64)
+    same = float(np.mean(codes == rc))
+    lg, lr = float(b["down"].loss.item()), ref["down"]["loss"]
+    say(f"mlp block: end-to-end down codes match {same:.5f}, loss {lg:.6g} vs {lr:.6g}")
+    assert same >= 0.95 and abs(lg - lr) <= 0.02 * lr
+    # X2 is the GPU's own down layer applied to the GPU's own X1 (a validity
+    # check on the CPU, fp16 output rounding and fp32 accumulation allowed)
+    Wd = O.model_weight_f16(b["down"].codes.cpu().numpy(), b["down"].scales.cpu().numpy(),
+                            b["down"].zeros.cpu().numpy(), group).astype(np.float64)
+    X2_own = b["X1"].cpu().numpy().astype(np.float64) @ Wd.T
+    assert rel_fro(b["X2"].cpu().numpy(), X2_own) < 2.0**-10
+    # and close to the oracle's block output: a fraction f of down codes one
+    # step off moves the output by about sqrt(f) * step / rms(What), 0.035 at
+    # f = 2% and 4-bit codes
+    ex2 = rel_fro(b["X2"].cpu().numpy(), ref["X2"])
+    say(f"mlp block: X2 rel fro {ex2:.3g}")
+    assert ex2 < 5e-2

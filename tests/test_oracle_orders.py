@@ -1,10 +1,13 @@
-"""Pins of the oracle's column-order variants: act-order and the greedy OBQ
-order (no GPU).
+"""Pins of the oracle's column-order variants (act-order and the greedy OBQ
+order) and of its calibration pipeline (layers sharing an input, an MLP
+block quantized layer by layer). No GPU.
 
 Each pin checks the oracle against something other than itself: a hand
 example, a pairwise restatement of the order, an invariance, the loss
-identity in the original coordinates, and a re-derivation of every greedy
-step with directly inverted sub-Hessians.
+identity in the original coordinates, a re-derivation of every greedy step
+with directly inverted sub-Hessians, propagated activations re-derived entry
+by entry, and planted mistakes (a wrong permutation composition,
+full-precision propagation) that the pins must catch.
 """
 
 import numpy as np
@@ -159,3 +162,67 @@ def test_obq_greedy_with_diagonal_hessian_is_round_to_nearest():
     ob = O.obq_greedy(W, H, 4, damp=0.0)
     codes, _, _ = O.rtn(W, 4, -1)
     assert np.array_equal(ob["codes"], codes)
+
+
+# ----------------------------------------------------------------------------
+# Calibration pipeline: layers sharing an input, and a block layer by layer
+# ----------------------------------------------------------------------------
+def test_shared_input_is_the_chunked_hessian_and_per_layer_sweeps():
+    X, _ = _xh(19, 120, 12)
+    Ws = [np.random.default_rng(20 + i).standard_normal((3 + i, 12)) for i in range(3)]
+    r = O.quantize_shared_input([X[:50], X[50:90], X[90:]], Ws, 3, 4, block=4, damp=0.02)
+    assert np.allclose(r["H"], 2.0 * X.T @ X, rtol=1e-12, atol=1e-12)
+    for W, layer in zip(Ws, r["layers"]):
+        one = O.quantize_layer(W, r["U"], 3, 4, block=4)
+        assert np.array_equal(layer["codes"], one["codes"]) and layer["loss"] == one["loss"]
+        # each layer's loss is its own output error on the shared input
+        assert layer["loss"] == pytest.approx(O.layer_loss_direct(X, W, layer["Wq"], r["lam"]), rel=1e-9)
+
+
+def test_model_weight_f16_rounds_the_float32_product():
+    codes = np.array([[0, 7, 3]])
+    s = np.array([[0.1]], np.float32)
+    z = np.array([[2]])
+    got = O.model_weight_f16(codes, s, z, -1)
+    want = np.array([np.float16(np.float32(0.1) * np.float32(k)) for k in (-2, 5, 1)])
+    assert got.dtype == np.float16 and np.array_equal(got[0], want)
+
+
+def _mlp(seed, n=160, d_model=16, d_ff=24):
+    r = np.random.default_rng(seed)
+    X0 = r.standard_normal((n, d_model)).astype(np.float16)
+    W_up = (0.3 * r.standard_normal((d_ff, d_model))).astype(np.float16)
+    W_down = (0.3 * r.standard_normal((d_model, d_ff))).astype(np.float16)
+    return X0, W_up, W_down
+
+
+def test_mlp_block_propagates_through_the_quantized_up_layer():
+    X0, W_up, W_down = _mlp(21)
+    b = O.quantize_mlp_block(X0, W_up, W_down, 4, 8, block=8, damp=0.02)
+    up, down = b["up"], b["down"]
+    # X1 entries re-derived one by one: relu of the dot product with the fp16 model weight
+    s32 = up["scales"].astype(np.float32)
+    for i, j in [(0, 0), (5, 3), (159, 23), (77, 11)]:
+        w = [np.float16(s32[j, c // 8] * np.float32(int(up["codes"][j, c]) - int(up["zeros"][j, c // 8])))
+             for c in range(16)]
+        dot = sum(float(X0[i, c]) * float(w[c]) for c in range(16))
+        assert b["X1"][i, j] == np.float16(max(dot, 0.0))
+    # each layer's loss is its output error on the input it was calibrated with
+    assert up["loss"] == pytest.approx(O.layer_loss_direct(X0, W_up, up["Wq"], up["lam"]), rel=1e-9)
+    assert down["loss"] == pytest.approx(O.layer_loss_direct(b["X1"], W_down, down["Wq"], down["lam"]), rel=1e-9)
+    # the block output is the quantized down layer applied to X1
+    Wd = O.model_weight_f16(down["codes"], down["scales"], down["zeros"], 8).astype(np.float64)
+    assert np.array_equal(b["X2"], (b["X1"].astype(np.float64) @ Wd.T).astype(np.float16))
+
+
+def test_mlp_block_down_hessian_is_not_from_full_precision_activations():
+    # Mutation: activations propagated through the unquantized up layer. The
+    # down layer's loss identity then fails, so the pin sees which input the
+    # down layer was calibrated with.
+    X0, W_up, W_down = _mlp(22)
+    b = O.quantize_mlp_block(X0, W_up, W_down, 3, 8, block=8, damp=0.02)
+    X1_fp = np.maximum(X0.astype(np.float64) @ W_up.astype(np.float64).T, 0.0).astype(np.float16)
+    assert not np.array_equal(X1_fp, b["X1"])
+    down = b["down"]
+    direct_fp = O.layer_loss_direct(X1_fp, W_down, down["Wq"], down["lam"])
+    assert abs(direct_fp - down["loss"]) > 1e-6 * down["loss"]
