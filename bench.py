@@ -242,6 +242,106 @@ def act_order_measure(g, torch, H, W, q_nat, cfg, ws_u, ws_q, steps=3):
     }
 
 
+def pipeline_measure(g, torch, X, W, cfg, steps=2):
+    """The calibration pipeline on the layer's activations X [N, d] (fp16):
+    (a) q/k/v sharing one Hessian and factor, their 3 d_row rows swept in one
+    call; (b) an MLP block d -> 11008 -> d quantized layer by layer, the down
+    layer calibrated on the quantized up layer's output. Weights beyond the
+    layer's own are seeded synthetic N(0, sigma^2) fp16. Every stage is timed
+    with HIP events on the current stream (1 untimed, `steps` timed runs)."""
+    import post_weight_quantization_17_amd.pipeline as P
+
+    dev = X.device
+    d = X.shape[1]
+    gen = torch.Generator(device=dev).manual_seed(7)
+    sig = cfg.w_sigma
+    Wk = (sig * torch.randn(W.shape, generator=gen, device=dev)).to(W.dtype)
+    Wv = (sig * torch.randn(W.shape, generator=gen, device=dev)).to(W.dtype)
+    d_ff = 11008
+    W_up = (sig * torch.randn((d_ff, d), generator=gen, device=dev)).to(torch.float16)
+    W_down = (sig * torch.randn((d, d_ff), generator=gen, device=dev)).to(torch.float16)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def qkv(e=None):
+        if e:
+            e[0].record()
+        H = g.gptq_hessian_accumulate(X)
+        if e:
+            e[1].record()
+        hv = g.gptq_prepare_hinv(H, cfg.damp)
+        if e:
+            e[2].record()
+        Wc = torch.cat([W, Wk, Wv], dim=0)
+        if e:
+            e[3].record()
+        q = g.gptq_quantize_layer(Wc, hv.U, cfg.bits, cfg.group_size, cfg.block)
+        if e:
+            e[4].record()
+        return q
+
+    qkv()
+    es = [[ev() for _ in range(5)] for _ in range(steps)]
+    for k in range(steps):
+        qkv(es[k])
+    torch.cuda.synchronize()
+    m = lambda e, i, j: float(np.mean([x[i].elapsed_time(x[j]) for x in e]))
+    qkv_ms = {"hessian": m(es, 0, 1), "prepare_hinv": m(es, 1, 2), "stack_rows": m(es, 2, 3),
+              "quantize_3_layers": m(es, 3, 4), "total": m(es, 0, 4)}
+
+    def block(e=None):
+        marks = []
+
+        def mark():
+            if e is not None:
+                t = ev()
+                t.record()
+                marks.append(t)
+
+        mark()
+        H_up = g.gptq_hessian_accumulate(X)
+        mark()
+        hv_up = g.gptq_prepare_hinv(H_up, cfg.damp)
+        mark()
+        q_up = g.gptq_quantize_layer(W_up, hv_up.U, cfg.bits, cfg.group_size, cfg.block)
+        mark()
+        Wh_up = g.gptq_dequantize(q_up.packed, q_up.scales, q_up.zeros, d, cfg.bits, cfg.group_size, torch.float16)
+        mark()
+        X1 = torch.matmul(X, Wh_up.t())
+        X1.relu_()
+        mark()
+        H_dn = g.gptq_hessian_accumulate(X1)
+        mark()
+        hv_dn = g.gptq_prepare_hinv(H_dn, cfg.damp)
+        mark()
+        q_dn = g.gptq_quantize_layer(W_down, hv_dn.U, cfg.bits, cfg.group_size, cfg.block)
+        mark()
+        Wh_dn = g.gptq_dequantize(q_dn.packed, q_dn.scales, q_dn.zeros, d_ff, cfg.bits, cfg.group_size, torch.float16)
+        mark()
+        X2 = torch.matmul(X1, Wh_dn.t())
+        mark()
+        if e is not None:
+            e.append(marks)
+        return hv_up, hv_dn, X2
+
+    hv_up, hv_dn, _ = block()
+    torch.cuda.synchronize()
+    if int(hv_up.info.item()) != 0 or int(hv_dn.info.item()) != 0:
+        raise RuntimeError("factorization failed in the MLP block")
+    runs = []
+    for _ in range(steps):
+        block(runs)
+    torch.cuda.synchronize()
+    names = ["hessian_up", "prepare_hinv_up", "quantize_up", "dequantize_up", "gemm_relu_up", "hessian_down",
+             "prepare_hinv_down", "quantize_down", "dequantize_down", "gemm_down"]
+    blk = {n: float(np.mean([r[i].elapsed_time(r[i + 1]) for r in runs])) for i, n in enumerate(names)}
+    blk["total"] = float(np.mean([r[0].elapsed_time(r[-1]) for r in runs]))
+    return {
+        "qkv_shared_input_ms": qkv_ms,
+        "mlp_block": {"d_model": d, "d_ff": d_ff, "tokens": X.shape[0], "stages_ms": blk},
+        "steps": steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +349,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="attn_proj_4096x4096_4bit_g128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only the layer path (no act-order, packed-product or pipeline legs)")
     ap.add_argument(
         "--copy-calibration",
         action="store_true",
@@ -387,13 +489,21 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    out["act_order"] = act_order_measure(g, torch, H, W, q, cfg, ws_u, ws_q)
-    ao = out["act_order"]
-    log(f"bench: act-order path after H {ao['ms_after_hessian']:.3f} ms {ao['stages_ms']}; "
-        f"loss {ao['loss_act_order']:.6g} (natural order {ao['loss_natural_order']:.6g})")
-    out["dequant_matvec"] = matvec_measure(g, torch, q, W, cfg)
-    log(f"bench: packed matrix-vector product {out['dequant_matvec']['us']:.2f} us "
-        f"({out['dequant_matvec']['gbps']:.0f} GB/s); dense fp16 {out['dequant_matvec']['fp16_dense_us']:.2f} us")
+    if not args.layer_only:
+        out["act_order"] = act_order_measure(g, torch, H, W, q, cfg, ws_u, ws_q)
+        ao = out["act_order"]
+        log(f"bench: act-order path after H {ao['ms_after_hessian']:.3f} ms {ao['stages_ms']}; "
+            f"loss {ao['loss_act_order']:.6g} (natural order {ao['loss_natural_order']:.6g})")
+        out["dequant_matvec"] = matvec_measure(g, torch, q, W, cfg)
+        log(f"bench: packed matrix-vector product {out['dequant_matvec']['us']:.2f} us "
+            f"({out['dequant_matvec']['gbps']:.0f} GB/s); dense fp16 {out['dequant_matvec']['fp16_dense_us']:.2f} us")
+        if X.dtype == torch.float16:
+            out["pipeline"] = pipeline_measure(g, torch, X, W, cfg)
+            pl = out["pipeline"]
+            log(f"bench: q/k/v sharing one Hessian {pl['qkv_shared_input_ms']['total']:.2f} ms "
+                f"{pl['qkv_shared_input_ms']}")
+            log(f"bench: MLP block layer by layer {pl['mlp_block']['stages_ms']['total']:.2f} ms "
+                f"{pl['mlp_block']['stages_ms']}")
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(cfg)
