@@ -40,6 +40,13 @@ constexpr int QB = 128;        // block width
 constexpr int QR = 16;         // rows per workgroup
 constexpr int QT = 256;        // threads per workgroup
 constexpr int QM = QB / 16;    // columns per lane per block
+// Whole-tile layers at least this tall and this wide take 32 rows per
+// workgroup. Measured: 49152 x 12288, 91.8 against 95-107 ms; 32768 x 8192,
+// 31.3 against 28.5 ms; 12288 x 12288, 28.9 against 27.0 ms. It pays only where
+// U (upper part 302 MB at d_col = 12288) does not stay in the last-level cache and
+// there are enough rows for full rounds of one-per-CU workgroups.
+constexpr int RG2_MIN_ROWS = 16384;
+constexpr int RG2_MIN_COLS = 12288;
 
 template <int Q, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -99,83 +106,100 @@ __device__ __forceinline__ float div_rn(float x, float s, float rs) {
 
 // Whole-tile form of the deferred update W[rows, i2:] -= E U[i1:i2, i2:]
 // (i2 = i1 + QB), used when the layer needs no bounds test anywhere:
-// d_col % 64 == 0, d_row % 16 == 0, W and U 16-byte aligned. Same MFMA
-// mapping as the checked form in the kernel below (the workgroup's 16 rows
-// are one v_mfma_f32_16x16x4f32 M tile, Es the A operand, U rows i1.. the B
-// operand; wave w takes the 64-column chunks i2 + 64 w + 256 c). With no
-// branches in the loop, the next chunk's W tile (the accumulators' start
-// value) and the U rows RING k-steps ahead, across chunk boundaries, stay in
-// flight while the current chunk's MFMAs run.
-template <typename WT>
+// d_col % 64 == 0, d_row a multiple of the workgroup's rows, W and U 16-byte
+// aligned. The workgroup's rows are RG v_mfma_f32_16x16x4f32 M tiles of 16
+// rows (Es the A operand) and U rows i1.. the B operand; wave w of the
+// 4 RG waves takes the 64-column chunks i2 + 64 w + 256 RG c and applies
+// all RG M tiles to each U operand it loads, so the U traffic per row falls
+// with RG. With no branches in the loop, the next chunk's W tiles (the
+// accumulators' start values) and the U rows RING k-steps ahead, across
+// chunk boundaries, stay in flight while the current chunk's MFMAs run.
+template <typename WT, int RG>
 __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, float* __restrict__ Wf,
                                                       const float* __restrict__ U, const float (*Es)[QB + 4],
                                                       int d_col, int row0, int i1, bool first) {
+  constexpr int NW = 4 * RG;  // waves per workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lk = lane >> 4;
   const int nb0 = i1 + QB + 64 * wave;
-  const int nch = nb0 < d_col ? (d_col - nb0 + 255) / 256 : 0;
+  const int nch = nb0 < d_col ? (d_col - nb0 + 64 * NW - 1) / (64 * NW) : 0;
   const size_t ustep = size_t(4) * d_col;
   const float* __restrict__ ub = U + size_t(i1 + lk) * d_col + nb0 + 4 * li;
-  const size_t wrow = size_t(row0 + 4 * lk) * d_col + nb0 + 4 * li;
-  auto ldb = [&](int ch, int t) -> floatx4 { return load4(ub + 256 * ch + t * ustep); };
-  auto ldw = [&](int ch, floatx4 (&v)[4]) {
+  size_t wrow[RG];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const size_t off = wrow + size_t(r) * d_col + 256 * ch;
-      v[r] = first ? load4(W + off) : load4(Wf + off);
-    }
+  for (int g = 0; g < RG; ++g) wrow[g] = size_t(row0 + 16 * g + 4 * lk) * d_col + nb0 + 4 * li;
+  auto ldb = [&](int ch, int t) -> floatx4 { return load4(ub + 64 * NW * ch + t * ustep); };
+  auto ldw = [&](int ch, floatx4 (&v)[RG][4]) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t off = wrow[g] + size_t(r) * d_col + 64 * NW * ch;
+        v[g][r] = first ? load4(W + off) : load4(Wf + off);
+      }
   };
-  constexpr int RING = 8;
-  constexpr int KS4 = QB / 4;  // k-steps per chunk
+  constexpr int RING = RG == 1 ? 8 : 4;  // U k-steps in flight (RG = 2: within 256 registers)
+  constexpr int KS4 = QB / 4;             // k-steps per chunk
   floatx4 ring[RING];
-  floatx4 wn[4];
+  floatx4 wn[RG][4];
   if (nch > 0) {
 #pragma unroll
     for (int t = 0; t < RING; ++t) ring[t] = ldb(0, t);
     ldw(0, wn);
   }
   for (int ch = 0; ch < nch; ++ch) {
-    floatx4 acc[4];
+    floatx4 acc[RG][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t][r] = wn[r][t];
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[g][t][r] = wn[g][r][t];
     const bool more = ch + 1 < nch;
     if (more) ldw(ch + 1, wn);
 #pragma unroll
     for (int t = 0; t < KS4; ++t) {
-      const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
       const floatx4 b = ring[t % RING];
       if (t + RING < KS4)
         ring[t % RING] = ldb(ch, t + RING);
       else if (more)
         ring[t % RING] = ldb(ch + 1, t + RING - KS4);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[v], 0, 0, 0);
+      for (int g = 0; g < RG; ++g) {
+        const float at = -Es[16 * g + li][4 * t + lk];  // A operand: row 16 g + li, k = 4t + lk
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[g][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[g][v], 0, 0, 0);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const size_t off = wrow + size_t(r) * d_col + 256 * ch;
-      *reinterpret_cast<float4*>(Wf + off) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
-    }
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const size_t off = wrow[g] + size_t(r) * d_col + 64 * NW * ch;
+        *reinterpret_cast<float4*>(Wf + off) = make_float4(acc[g][0][r], acc[g][1][r], acc[g][2][r], acc[g][3][r]);
+      }
   }
 }
 
-template <typename WT, bool WHOLE>
-__global__ void __launch_bounds__(QT, 2)
+// RG row groups of QR rows per workgroup (QT threads each). RG > 1 only for
+// the whole-tile form.
+template <typename WT, bool WHOLE, int RG>
+__global__ void __launch_bounds__(QT * RG, RG == 1 ? 2 : 1)
 gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __restrict__ U, int d_row, int d_col,
            int bits, int sym, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
            int32_t* __restrict__ zeros, uint32_t* __restrict__ packed, int nwords, float* __restrict__ row_loss,
            double* __restrict__ wg_loss) {
+  static_assert(WHOLE || RG == 1, "the checked form takes one row group");
+  constexpr int NT = QT * RG, NR = QR * RG;  // threads and rows per workgroup
   __shared__ __attribute__((aligned(16))) float Ud[QB][QB];
-  __shared__ float Es[QR][QB + 4];
-  __shared__ uint8_t Cs[QR][QB];
-  __shared__ double Lsum[QR];
+  __shared__ float Es[NR][QB + 4];
+  __shared__ uint8_t Cs[NR][QB];
+  __shared__ double Lsum[NR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rloc = wave * 4 + (lane >> 4);
   const int sub = lane & 15;
-  const int row0 = blockIdx.x * QR;
+  const int row0 = blockIdx.x * NR;
   const int row = row0 + rloc;
   const bool row_ok = row < d_row;
   const size_t rbase = size_t(row) * d_col;
@@ -208,18 +232,20 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
 
     // 1. U block (upper part; padded columns act as identity rows) and W block.
     if (vec4 && nvalid == QB) {
-      // Full aligned block: 2 x 8 float4 loads per thread, each batch in
-      // flight before its LDS stores; the strict lower triangle is zeroed.
+      // Full aligned block: 32 threads per row of 128 floats, NT / 32 rows
+      // per pass, batches of 8 float4 loads in flight before their LDS
+      // stores; the strict lower triangle is zeroed.
+      constexpr int RP = NT / 32, NPT = QB / RP;  // rows per pass, rows per thread
       const int k0 = tid >> 5, j0 = (tid & 31) * 4;
       const float* src = U + size_t(i1 + k0) * d_col + i1 + j0;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int half = 0; half < NPT / 8; ++half) {
         floatx4 uv[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) uv[t] = load4(src + size_t(8 * (t + 8 * half)) * d_col);
+        for (int t = 0; t < 8; ++t) uv[t] = load4(src + size_t(RP * (t + 8 * half)) * d_col);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int k = k0 + 8 * (t + 8 * half);
+          const int k = k0 + RP * (t + 8 * half);
           floatx4 v = uv[t];
 #pragma unroll
           for (int u = 0; u < 4; ++u) v[u] = (j0 + u >= k) ? v[u] : 0.f;
@@ -227,7 +253,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
         }
       }
     } else {
-      for (int e = tid; e < QB * QB; e += QT) {
+      for (int e = tid; e < QB * QB; e += NT) {
         const int k = e >> 7, j = e & (QB - 1);
         float v;
         if (k < nvalid && j < nvalid)
@@ -333,8 +359,9 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
 
     // 4. Deferred update of the later columns: W[:, i2:] -= E U[blk, i2:].
     const int i2 = i1 + QB;
-    if (WHOLE && i2 < d_col) trailing_update_whole(W, Wf, U, Es, d_col, row0, i1, first);
-    if (!WHOLE && i2 < d_col) {
+    if constexpr (WHOLE) {
+      if (i2 < d_col) trailing_update_whole<WT, RG>(W, Wf, U, Es, d_col, row0, i1, first);
+    } else if (i2 < d_col) {
       const int li = lane & 15, lk = lane >> 4;
       for (int n0 = i2 + 64 * wave; n0 < d_col; n0 += 256) {
         const int col = n0 + 4 * li;
@@ -410,7 +437,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
   __syncthreads();
   if (tid == 0) {
     double t = 0.0;
-    for (int r = 0; r < QR; ++r) t += Lsum[r];
+    for (int r = 0; r < NR; ++r) t += Lsum[r];
     wg_loss[blockIdx.x] = t;
   }
 }
@@ -493,23 +520,25 @@ extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int
   hipStream_t s = as_stream(stream);
   const int ngroups = group_size == -1 ? 1 : int((d_col + group_size - 1) / group_size);
   const int nwords = int((d_col * bits + 31) / 32);
-  const unsigned nwg = unsigned((d_row + QR - 1) / QR);
   const int esz = wdtype == GPTQ_F16 ? 2 : 4;
   const int vec4 = (d_col % 4 == 0) && (reinterpret_cast<uintptr_t>(W) % (4 * esz) == 0) &&
                    (reinterpret_cast<uintptr_t>(U) % 16 == 0) ? 1 : 0;
   // Whole-tile layers (every chunk of the deferred update complete, every
-  // workgroup's 16 rows present) take the branch-free update.
+  // workgroup's rows present) take the branch-free update; tall and wide ones
+  // take 32 rows per workgroup, halving the U rows each row's update streams.
   const bool whole = vec4 && d_col % 64 == 0 && d_row % QR == 0;
+  const int rg = (whole && d_row % (2 * QR) == 0 && d_row >= RG2_MIN_ROWS && d_col >= RG2_MIN_COLS) ? 2 : 1;
+  const unsigned nwg = unsigned((d_row + rg * QR - 1) / (rg * QR));
   if (wdtype == GPTQ_F16) {
-    auto k = whole ? gptq_sweep<__half, true> : gptq_sweep<__half, false>;
-    hipLaunchKernelGGL(k, dim3(nwg), dim3(QT), 0, s, static_cast<const __half*>(W), w.Wf, U, int(d_row), int(d_col),
-                       bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
-                       w.wg_loss);
+    auto k = rg == 2 ? gptq_sweep<__half, true, 2> : whole ? gptq_sweep<__half, true, 1> : gptq_sweep<__half, false, 1>;
+    hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * QT), 0, s, static_cast<const __half*>(W), w.Wf, U, int(d_row),
+                       int(d_col), bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords,
+                       row_loss, w.wg_loss);
   } else {
-    auto k = whole ? gptq_sweep<float, true> : gptq_sweep<float, false>;
-    hipLaunchKernelGGL(k, dim3(nwg), dim3(QT), 0, s, static_cast<const float*>(W), w.Wf, U, int(d_row), int(d_col),
-                       bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords, row_loss,
-                       w.wg_loss);
+    auto k = rg == 2 ? gptq_sweep<float, true, 2> : whole ? gptq_sweep<float, true, 1> : gptq_sweep<float, false, 1>;
+    hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * QT), 0, s, static_cast<const float*>(W), w.Wf, U, int(d_row),
+                       int(d_col), bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords,
+                       row_loss, w.wg_loss);
   }
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   hipLaunchKernelGGL(loss_final, dim3(1), dim3(256), 0, s, w.wg_loss, int(nwg), loss);

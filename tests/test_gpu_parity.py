@@ -259,6 +259,29 @@ def test_quantize_is_deterministic(gpu):
 
 
 # -------------------------------------------------------------------- pack
+@pytest.mark.parametrize("wdt,bits,group", [(np.float16, 3, 128), (np.float32, 4, -1)])
+def test_tall_layer_row_groups_are_bit_identical(gpu, wdt, bits, group):
+    """Tile-aligned layers with at least 16384 rows (a multiple of 32) and
+    12288 columns take 32 rows per workgroup, others 16. A row's arithmetic
+    is the same either way, so the 16384-row layer and the same layer one
+    16-row group shorter agree bit for bit on the rows both have; the tall
+    one also matches the oracle on sampled rows. U is any upper-triangular
+    factor with a positive diagonal (both sides take it as given)."""
+    d_row, d_col = 16384, 12288
+    r = np.random.default_rng(98)
+    U = (np.triu(r.standard_normal((d_col, d_col), dtype=np.float32)) * 1e-3 + np.eye(d_col, dtype=np.float32))
+    W = (0.02 * r.standard_normal((d_row, d_col), dtype=np.float32)).astype(wdt)
+    Ud, Wd = gpu_tensor(U), gpu_tensor(W)
+    qa = gpu.gptq_quantize_layer(Wd, Ud, bits, group, 128)
+    qb = gpu.gptq_quantize_layer(Wd[: d_row - 16].contiguous(), Ud, bits, group, 128)
+    torch.cuda.synchronize()
+    for name in ("codes", "scales", "zeros", "packed", "row_loss"):
+        assert torch.equal(getattr(qa, name)[: d_row - 16], getattr(qb, name)), name
+    rows = np.unique(np.append(r.choice(d_row, 24, replace=False), [0, 31, d_row - 1]))
+    ref = O.quantize_layer(W[rows], U.astype(np.float64), bits, group, 128, decide=np.float32)
+    check_quant(qa, ref, bits, rows=rows)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("d_row,d_col", [(1, 1), (3, 10), (7, 11), (5, 128), (9, 1000)])
 def test_pack_parity(gpu, bits, d_row, d_col):
