@@ -359,6 +359,157 @@ __global__ void __launch_bounds__(256) dequant_matvec_pairs(const PairArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MFMA form, for d_col % 128 == 0, groups of a multiple of 128 columns (or one
+// group per row), 16-byte aligned x rows, up to 16 vectors per pass.
+//
+// A wave takes 16 rows; lane l handles row l % 16 and unit slot q = l / 16
+// of each 128-column super-unit (4 units of 32 codes, one group). For each
+// of the super-unit's 4 code chunks t, a lane's 4 code pairs (plan pairs
+// 4t .. 4t+3 of its unit) become the 8 halves of the B operand of
+// v_mfma_f32_16x16x32_f16, already as exact fp16 values code - z (the
+// packed FMA's offset carries -1024 2^-o - z); the A operand is the same 4
+// pairs of activations for vector l % 16, read from LDS, where the
+// workgroup has staged them in pair order. So D[m][n] = sum over the
+// super-unit of x_m (code - z)_n, and y[m][n] += s_n D[m][n] once per
+// super-unit. The dot products run on the matrix core; the VALU only cuts
+// and converts codes. Cutting and converting dominates either way, so for one
+// or two vectors the pair kernel is faster (its loads read whole lines of one
+// row); with more vectors this form takes 16 per pass against 2.
+constexpr int MM_WAVES = 4;  // waves per workgroup, 16 rows each
+constexpr int MM_CH = 8;     // super-units per LDS chunk: 8 x 4 KB of staged activations
+constexpr int MM_MIN_BATCH = 3;  // one or two vectors: the pair kernel is faster (measured)
+
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+
+// The 4 code pairs of chunk t of a unit as the B operand (code - z, fp16).
+template <int BITS, int T>
+__device__ __forceinline__ half8 mm_codes(const uint32_t (&w)[BITS], const PairMasks<BITS>& pm, h2_t zz) {
+  using PL = PairPlan<BITS>;
+  h2_t c[4];
+  static_for<0, 4>([&](auto pc) {
+    constexpr int i = 4 * T + decltype(pc)::value;
+    constexpr int olo = PL::o_lo(i), ohi = PL::o_hi(i);
+    const uint32_t t = (unit_window<BITS, PL::win(i)>(w) & pm.m[i]) | pm.magic;  // 1024 + (code << o) per half
+    const h2_t sc = {(_Float16)(1.0f / float(1 << olo)), (_Float16)(1.0f / float(1 << ohi))};
+    const h2_t base = {(_Float16)(-1024.0f / float(1 << olo)), (_Float16)(-1024.0f / float(1 << ohi))};
+    const h2_t of = base - zz;  // -1024 2^-o - z, exact in fp16
+    c[decltype(pc)::value] = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, t), sc, of);  // code - z, exact
+  });
+  const h4_t lo = __builtin_shufflevector(c[0], c[1], 0, 1, 2, 3);
+  const h4_t hi = __builtin_shufflevector(c[2], c[3], 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Staging of one LDS entry: the 4 activation pairs of chunk t of unit q of a
+// super-unit for vector m, from the 8 activations that chunk needs (one
+// 16-byte run, or two 8-byte runs for 2-bit codes), in plan order.
+template <int BITS>
+__device__ __forceinline__ uint4 mm_stage(const __half* __restrict__ xr, int col0, int t) {
+  uint32_t a[4];
+  if constexpr (BITS == 2) {
+    const int base = col0 + 16 * (t >> 1) + 4 * (t & 1);
+    const uint2 lo = *reinterpret_cast<const uint2*>(xr + base);
+    const uint2 hi = *reinterpret_cast<const uint2*>(xr + base + 8);
+    a[0] = lo.x;
+    a[1] = lo.y;
+    a[2] = hi.x;
+    a[3] = hi.y;
+  } else {
+    const uint4 v = *reinterpret_cast<const uint4*>(xr + col0 + 8 * t);
+    a[0] = v.x;
+    a[1] = v.y;
+    a[2] = v.z;
+    a[3] = v.w;
+  }
+  // halves X0..X7 = a[0].lo, a[0].hi, a[1].lo, ...
+  h2_t X[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) X[k] = __builtin_bit_cast(h2_t, a[k]);
+  h2_t p[4];
+  if constexpr (BITS == 8) {  // (X0, X2), (X1, X3), (X4, X6), (X5, X7)
+    p[0] = __builtin_shufflevector(X[0], X[1], 0, 2);
+    p[1] = __builtin_shufflevector(X[0], X[1], 1, 3);
+    p[2] = __builtin_shufflevector(X[2], X[3], 0, 2);
+    p[3] = __builtin_shufflevector(X[2], X[3], 1, 3);
+  } else {  // (X0, X4), (X1, X5), (X2, X6), (X3, X7)
+    p[0] = __builtin_shufflevector(X[0], X[2], 0, 2);
+    p[1] = __builtin_shufflevector(X[0], X[2], 1, 3);
+    p[2] = __builtin_shufflevector(X[1], X[3], 0, 2);
+    p[3] = __builtin_shufflevector(X[1], X[3], 1, 3);
+  }
+  return make_uint4(__builtin_bit_cast(uint32_t, p[0]), __builtin_bit_cast(uint32_t, p[1]),
+                    __builtin_bit_cast(uint32_t, p[2]), __builtin_bit_cast(uint32_t, p[3]));
+}
+
+// Rows past d_row read row d_row - 1 and store nothing; vectors past `batch`
+// are staged as zeros and stored nowhere.
+template <int BITS>
+__global__ void __launch_bounds__(64 * MM_WAVES)
+dequant_matmul_mfma(const uint32_t* __restrict__ packed, const float* __restrict__ scales,
+                    const int32_t* __restrict__ zeros, int d_row, int d_col, int nwords, int group, int ngroups,
+                    const __half* __restrict__ x, int64_t ldx, int batch, float* __restrict__ y, int64_t ldy) {
+  __shared__ uint4 xs[MM_CH * 4 * 4 * 16];  // [super-unit][chunk t][unit q][vector m]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, q = lane >> 4;
+  const int row = blockIdx.x * (16 * MM_WAVES) + wave * 16 + n;
+  const int rrow = row < d_row ? row : d_row - 1;
+  const uint32_t* __restrict__ pr = packed + size_t(rrow) * nwords;
+  const float* __restrict__ sr = scales + size_t(rrow) * ngroups;
+  const int32_t* __restrict__ zr = zeros + size_t(rrow) * ngroups;
+  const PairMasks<BITS> pm = pair_masks<BITS>();
+  const int nsu = d_col >> 7;
+  const int su_per_group = group > 0 ? group >> 7 : nsu;  // super-units per group
+  floatx4 Y = {0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = 0; c0 < nsu; c0 += MM_CH) {
+    const int nch = nsu - c0 < MM_CH ? nsu - c0 : MM_CH;
+    __syncthreads();  // the previous chunk's entries are no longer read
+    for (int e = tid; e < nch * 256; e += 64 * MM_WAVES) {
+      const int sl = e >> 8, t = (e >> 6) & 3, qq = (e >> 4) & 3, m = e & 15;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (m < batch) v = mm_stage<BITS>(x + m * ldx, 128 * (c0 + sl) + 32 * qq, t);
+      xs[e] = v;
+    }
+    __syncthreads();
+    uint32_t w[BITS], wn[BITS];
+    const int u0 = 4 * c0 + q;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) w[k] = pr[u0 * BITS + k];
+    for (int sl = 0; sl < nch; ++sl) {
+      const int su = c0 + sl;
+      // next super-unit's words (the last one re-read, unused), issued before this one is converted
+      const int un = 4 * (sl + 1 < nch ? su + 1 : su) + q;
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) wn[k] = pr[un * BITS + k];
+      const int gi = su / su_per_group;
+      const float sv = sr[gi];
+      const _Float16 zh = (_Float16)float(zr[gi]);
+      const h2_t zz = {zh, zh};
+      floatx4 D = {0.f, 0.f, 0.f, 0.f};
+      const uint4* xa = xs + (sl * 4) * 64 + q * 16 + n;  // entry (sl, t, q, m = n) at xa + 64 t
+      static_for<0, 4>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        const half8 b = mm_codes<BITS, t>(w, pm, zz);
+        const half8 a = __builtin_bit_cast(half8, xa[64 * t]);
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, D, 0, 0, 0);
+      });
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Y[r] = fmaf(sv, D[r], Y[r]);
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) w[k] = wn[k];
+    }
+  }
+  // lane l holds y[m = 4 q + r][row]: D rows are the vectors, columns the rows
+  if (row < d_row) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * q + r;
+      if (m < batch) y[m * ldy + row] = Y[r];
+    }
+  }
+}
+
 template <int BITS, int NB, bool VECX>
 __global__ void __launch_bounds__(256)
 dequant_matvec_kernel(const uint32_t* __restrict__ packed, const float* __restrict__ scales,
@@ -477,6 +628,15 @@ int launch_nb(bool vecx, const uint32_t* packed, const float* scales, const int3
   return launch_status();
 }
 
+template <int BITS>
+int launch_mfma(const uint32_t* packed, const float* scales, const int32_t* zeros, int d_row, int d_col, int nwords,
+                int group, int ngroups, const __half* x, int64_t ldx, int batch, float* y, int64_t ldy, hipStream_t s) {
+  const dim3 grid(unsigned((d_row + 16 * MM_WAVES - 1) / (16 * MM_WAVES))), block(64 * MM_WAVES);
+  hipLaunchKernelGGL((dequant_matmul_mfma<BITS>), grid, block, 0, s, packed, scales, zeros, d_row, d_col, nwords, group,
+                     ngroups, x, ldx, batch, y, ldy);
+  return launch_status();
+}
+
 template <int BITS, int RB, int NB>
 int launch_pairs_rb(const uint32_t* packed, const float* scales, const int32_t* zeros, int d_row, int d_col,
                     int nwords, float inv_upg, int ngroups, const __half* x, int64_t ldx, float* y, int64_t ldy,
@@ -587,6 +747,37 @@ extern "C" int gptq_dequant_matvec(const uint32_t* packed, const float* scales, 
   const int grp = group_size == -1 ? 0 : int(group_size);
   const bool vecx = (ldx % 8 == 0) && (reinterpret_cast<uintptr_t>(x) % 16 == 0);
   const bool pairs = vecx && (group_size == -1 || group_size % 32 == 0);
+  // The MFMA form needs whole 128-column super-units inside one group; it
+  // takes up to 16 vectors per pass, where the pair kernel takes 2.
+  const bool mfma = vecx && d_col % 128 == 0 && (group_size == -1 || group_size % 128 == 0) && batch >= MM_MIN_BATCH;
+  if (mfma) {
+    hipStream_t s = as_stream(stream);
+    const __half* xh = static_cast<const __half*>(x);
+    for (int64_t b0 = 0; b0 < batch; b0 += 16) {
+      const int nb = int(batch - b0 < 16 ? batch - b0 : 16);
+      int st;
+      switch (bits) {
+        case 2:
+          st = launch_mfma<2>(packed, scales, zeros, int(d_row), int(d_col), nwords, grp, ngroups, xh + b0 * ldx, ldx,
+                              nb, y + b0 * d_row, d_row, s);
+          break;
+        case 3:
+          st = launch_mfma<3>(packed, scales, zeros, int(d_row), int(d_col), nwords, grp, ngroups, xh + b0 * ldx, ldx,
+                              nb, y + b0 * d_row, d_row, s);
+          break;
+        case 4:
+          st = launch_mfma<4>(packed, scales, zeros, int(d_row), int(d_col), nwords, grp, ngroups, xh + b0 * ldx, ldx,
+                              nb, y + b0 * d_row, d_row, s);
+          break;
+        default:
+          st = launch_mfma<8>(packed, scales, zeros, int(d_row), int(d_col), nwords, grp, ngroups, xh + b0 * ldx, ldx,
+                              nb, y + b0 * d_row, d_row, s);
+          break;
+      }
+      if (st != GPTQ_OK) return st;
+    }
+    return GPTQ_OK;
+  }
   hipStream_t s = as_stream(stream);
   const __half* xh = static_cast<const __half*>(x);
   for (int64_t b0 = 0; b0 < batch;) {

@@ -78,6 +78,16 @@ def run(gpu, d_row, d_col, bits, group, batch, seed, ldx=None, off=1):
         # more row blocks than resident waves: several row blocks per wave
         (20000, 512, 4, 128, 1),
         (40000, 264, 2, -1, 2),
+        # the MFMA form (128-column super-units, groups of 128-multiples, more
+        # than two vectors or tall layers): a ragged last group of 256, rows
+        # not a multiple of 64, exactly 16 and 17 vectors (two passes), an
+        # LDS chunk boundary (9 super-units), every code width
+        (100, 640, 2, 256, 5),
+        (70, 1024, 8, -1, 16),
+        (50, 512, 3, 128, 17),
+        (9000, 1152, 4, 128, 1),
+        (8192, 1024, 2, 128, 1),
+        (300, 2048, 8, 128, 3),
     ],
 )
 def test_dequant_matvec_parity(gpu, d_row, d_col, bits, group, batch):
@@ -92,6 +102,7 @@ def test_dequant_matvec_strided_aligned_activations(gpu):
     # 16-byte aligned rows ldx apart: the code-pair kernel with ldx != d_col
     run(gpu, 64, 1000, 3, -1, 3, seed=6, ldx=1040, off=8)
     run(gpu, 64, 1024, 4, 128, 2, seed=7, ldx=1032, off=8)
+    run(gpu, 64, 1024, 3, 128, 5, seed=8, ldx=1040, off=8)  # the MFMA form
 
 
 def test_dequant_matvec_rejects_bad_arguments(gpu):
