@@ -235,11 +235,12 @@ int gptq_gather(const void* src, int elem_bytes, int64_t src_rows, int64_t src_c
  *   x          device fp16, batch rows of d_col values, row stride ldx >= d_col.
  *   y          device fp32, batch x d_row, row-major.
  * fp32 accumulation of exact codes times fp16 activations; the per-row sum
- * over lanes has a fixed order, so results are deterministic. When
- * group_size is -1 or a multiple of 32 and x rows are 16-byte aligned
- * (ldx % 8 == 0, x 16-byte aligned), a faster kernel runs (two codes per
- * instruction, several rows per wave); other layouts take a per-code
- * kernel. Runs on `stream` (NULL: the default stream); nothing is
+ * has a fixed order, so results are deterministic. When group_size is -1 or
+ * a multiple of 32 and x rows are 16-byte aligned (ldx % 8 == 0, x 16-byte
+ * aligned), a faster kernel runs (two codes per instruction, several rows
+ * per wave); with 3 or more vectors, d_col a multiple of 128 and groups of
+ * 128-column multiples (or -1), up to 16 vectors go through fp16 MFMAs per
+ * pass; other layouts take a per-code kernel. Runs on `stream` (NULL: the default stream); nothing is
  * allocated. Errors: sizes < 1, NULL pointers, ldx < d_col, bad bits or
  * group -> GPTQ_E_INVALID_ARG; a failed launch or device query ->
  * GPTQ_E_HIP.

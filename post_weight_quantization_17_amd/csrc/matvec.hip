@@ -10,7 +10,7 @@
 //
 //   Y[b][r] = sum_c X[b][c] * s[r][g(c)] * (code[r][c] - z[r][g(c)])
 //
-// Design (gfx950). Two kernels:
+// Design (gfx950). Three kernels:
 //
 // * dequant_matvec_pairs, for groups that are a multiple of 32 columns (or
 //   one group per row) and 16-byte aligned activations: the 32-column unit
@@ -27,6 +27,10 @@
 //   activation pairs and the unit's activation sum are built once for RB
 //   rows; the next unit's loads are in flight while one unit is computed.
 //   The zero is folded as s (sum c x - z sum x) per unit.
+// * dequant_matmul_mfma, for 3 to 16 vectors per pass (d_col a multiple of
+//   128, groups of 128-column multiples or one per row, aligned x): the
+//   codes, cut with the same pair plan and already as code - z, are the B
+//   operand of fp16 MFMAs, the activations the A operand (see below).
 // * dequant_matvec_kernel, for every other case: one wave per row, codes
 //   extracted one at a time and the fold taken per 8-column chunk.
 //
