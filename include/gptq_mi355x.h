@@ -240,10 +240,10 @@ int gptq_gather(const void* src, int elem_bytes, int64_t src_rows, int64_t src_c
  * aligned), a faster kernel runs (two codes per instruction, several rows
  * per wave); with 3 or more vectors, d_col a multiple of 128 and groups of
  * 128-column multiples (or -1), up to 16 vectors go through fp16 MFMAs per
- * pass; other layouts take a per-code kernel. Runs on `stream` (NULL: the default stream); nothing is
- * allocated. Errors: sizes < 1, NULL pointers, ldx < d_col, bad bits or
- * group -> GPTQ_E_INVALID_ARG; a failed launch or device query ->
- * GPTQ_E_HIP.
+ * pass; other layouts take a per-code kernel. Runs on `stream` (NULL: the
+ * default stream); nothing is allocated. Errors: sizes < 1, NULL pointers,
+ * ldx < d_col, bad bits or group -> GPTQ_E_INVALID_ARG; a failed launch or
+ * device query -> GPTQ_E_HIP.
  * ---------------------------------------------------------------------- */
 int gptq_dequant_matvec(const uint32_t* packed, const float* scales, const int32_t* zeros,
                         int64_t d_row, int64_t d_col, int bits, int64_t group_size, const void* x,
