@@ -47,6 +47,9 @@ constexpr int QM = QB / 16;    // columns per lane per block
 // there are enough rows for full rounds of one-per-CU workgroups.
 constexpr int RG2_MIN_ROWS = 16384;
 constexpr int RG2_MIN_COLS = 12288;
+// Whole-tile layers of at most this many 16-row workgroups (one per CU)
+// take 8 waves per workgroup.
+constexpr int XW2_MAX_WG = 256;
 
 template <int Q, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -109,16 +112,16 @@ __device__ __forceinline__ float div_rn(float x, float s, float rs) {
 // d_col % 64 == 0, d_row a multiple of the workgroup's rows, W and U 16-byte
 // aligned. The workgroup's rows are RG v_mfma_f32_16x16x4f32 M tiles of 16
 // rows (Es the A operand) and U rows i1.. the B operand; wave w of the
-// 4 RG waves takes the 64-column chunks i2 + 64 w + 256 RG c and applies
-// all RG M tiles to each U operand it loads, so the U traffic per row falls
-// with RG. With no branches in the loop, the next chunk's W tiles (the
+// NW = 4 RG XW waves takes the 64-column chunks i2 + 64 w + 64 NW c and
+// applies all RG M tiles to each U operand it loads, so the U traffic per
+// row falls with RG (XW > 1 only adds waves to this update). With no branches in the loop, the next chunk's W tiles (the
 // accumulators' start values) and the U rows RING k-steps ahead, across
 // chunk boundaries, stay in flight while the current chunk's MFMAs run.
-template <typename WT, int RG>
+template <typename WT, int RG, int XW>
 __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, float* __restrict__ Wf,
                                                       const float* __restrict__ U, const float (*Es)[QB + 4],
                                                       int d_col, int row0, int i1, bool first) {
-  constexpr int NW = 4 * RG;  // waves per workgroup
+  constexpr int NW = 4 * RG * XW;  // waves per workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lk = lane >> 4;
   const int nb0 = i1 + QB + 64 * wave;
@@ -181,27 +184,30 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
   }
 }
 
-// RG row groups of QR rows per workgroup (QT threads each). RG > 1 only for
-// the whole-tile form.
-template <typename WT, bool WHOLE, int RG>
-__global__ void __launch_bounds__(QT * RG, RG == 1 ? 2 : 1)
+// RG row groups of QR rows per workgroup (QT threads each), and XW times as
+// many waves in the deferred update: with XW = 2 the waves beyond the row
+// groups' 4 RG take part only in that update (and in the workgroup's
+// barriers). RG > 1 and XW > 1 only for the whole-tile form.
+template <typename WT, bool WHOLE, int RG, int XW>
+__global__ void __launch_bounds__(QT * RG * XW, RG * XW == 1 ? 2 : 1)
 gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __restrict__ U, int d_row, int d_col,
            int bits, int sym, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
            int32_t* __restrict__ zeros, uint32_t* __restrict__ packed, int nwords, float* __restrict__ row_loss,
            double* __restrict__ wg_loss) {
-  static_assert(WHOLE || RG == 1, "the checked form takes one row group");
-  constexpr int NT = QT * RG, NR = QR * RG;  // threads and rows per workgroup
+  static_assert(WHOLE || (RG == 1 && XW == 1), "the checked form takes one row group of 4 waves");
+  constexpr int NT = QT * RG * XW, NR = QR * RG;  // threads and rows per workgroup
   __shared__ __attribute__((aligned(16))) float Ud[QB][QB];
   __shared__ float Es[NR][QB + 4];
   __shared__ uint8_t Cs[NR][QB];
   __shared__ double Lsum[NR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rloc = wave * 4 + (lane >> 4);
+  const bool rows_wave = wave < 4 * RG;  // wave-uniform: this wave carries rows
+  const int rloc = rows_wave ? wave * 4 + (lane >> 4) : 0;
   const int sub = lane & 15;
   const int row0 = blockIdx.x * NR;
   const int row = row0 + rloc;
-  const bool row_ok = row < d_row;
+  const bool row_ok = rows_wave && row < d_row;
   const size_t rbase = size_t(row) * d_col;
   const float maxq = float((1 << bits) - 1);
   const float qs = float((1 << (bits - 1)) - 1), zs = float(1 << (bits - 1));
@@ -284,7 +290,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
     float uc[QM], un[QM];
 #pragma unroll
     for (int mm = 0; mm < QM; ++mm) uc[mm] = Ud[0][16 * mm + sub];
-    static_for<0, QB>([&](auto qc) {
+    if (rows_wave) static_for<0, QB>([&](auto qc) {
       constexpr int q = decltype(qc)::value;
       constexpr int m = q / 16;
       constexpr int o = q % 16;
@@ -360,7 +366,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
     // 4. Deferred update of the later columns: W[:, i2:] -= E U[blk, i2:].
     const int i2 = i1 + QB;
     if constexpr (WHOLE) {
-      if (i2 < d_col) trailing_update_whole<WT, RG>(W, Wf, U, Es, d_col, row0, i1, first);
+      if (i2 < d_col) trailing_update_whole<WT, RG, XW>(W, Wf, U, Es, d_col, row0, i1, first);
     } else if (i2 < d_col) {
       const int li = lane & 15, lk = lane >> 4;
       for (int n0 = i2 + 64 * wave; n0 < d_col; n0 += 256) {
@@ -430,7 +436,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
     __syncthreads();
   }
 
-  if (sub == 0) {
+  if (sub == 0 && rows_wave) {
     Lsum[rloc] = row_ok ? lacc : 0.0;
     if (row_ok && row_loss) row_loss[row] = float(lacc);
   }
@@ -529,14 +535,23 @@ extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int
   const bool whole = vec4 && d_col % 64 == 0 && d_row % QR == 0;
   const int rg = (whole && d_row % (2 * QR) == 0 && d_row >= RG2_MIN_ROWS && d_col >= RG2_MIN_COLS) ? 2 : 1;
   const unsigned nwg = unsigned((d_row + rg * QR - 1) / (rg * QR));
+  // Layers small enough that every CU holds at most one 16-row workgroup
+  // give it 8 waves: the extra 4 work only in the deferred update.
+  const int xw = (whole && rg == 1 && nwg <= XW2_MAX_WG) ? 2 : 1;
   if (wdtype == GPTQ_F16) {
-    auto k = rg == 2 ? gptq_sweep<__half, true, 2> : whole ? gptq_sweep<__half, true, 1> : gptq_sweep<__half, false, 1>;
-    hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * QT), 0, s, static_cast<const __half*>(W), w.Wf, U, int(d_row),
+    auto k = rg == 2 ? gptq_sweep<__half, true, 2, 1>
+             : xw == 2 ? gptq_sweep<__half, true, 1, 2>
+             : whole ? gptq_sweep<__half, true, 1, 1>
+                     : gptq_sweep<__half, false, 1, 1>;
+    hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * xw * QT), 0, s, static_cast<const __half*>(W), w.Wf, U, int(d_row),
                        int(d_col), bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords,
                        row_loss, w.wg_loss);
   } else {
-    auto k = rg == 2 ? gptq_sweep<float, true, 2> : whole ? gptq_sweep<float, true, 1> : gptq_sweep<float, false, 1>;
-    hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * QT), 0, s, static_cast<const float*>(W), w.Wf, U, int(d_row),
+    auto k = rg == 2 ? gptq_sweep<float, true, 2, 1>
+             : xw == 2 ? gptq_sweep<float, true, 1, 2>
+             : whole ? gptq_sweep<float, true, 1, 1>
+                     : gptq_sweep<float, false, 1, 1>;
+    hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * xw * QT), 0, s, static_cast<const float*>(W), w.Wf, U, int(d_row),
                        int(d_col), bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords,
                        row_loss, w.wg_loss);
   }

@@ -282,6 +282,25 @@ def test_tall_layer_row_groups_are_bit_identical(gpu, wdt, bits, group):
     check_quant(qa, ref, bits, rows=rows)
 
 
+@pytest.mark.parametrize("wdt,bits,group", [(np.float16, 4, 128), (np.float32, 3, -1)])
+def test_small_layer_update_waves_are_bit_identical(gpu, wdt, bits, group):
+    """Tile-aligned layers of at most 256 workgroups (4096 rows) run 8 waves
+    per workgroup, the extra 4 only in the deferred update; with one more
+    16-row group the layer runs 4. The shared rows agree bit for bit."""
+    d_col = 512
+    U = oracle_u(d_col, 96)
+    W = (0.02 * np.random.default_rng(95).standard_normal((4112, d_col))).astype(wdt)
+    Ud, Wd = gpu_tensor(U), gpu_tensor(W)
+    qa = gpu.gptq_quantize_layer(Wd[:4096].contiguous(), Ud, bits, group, 128)
+    qb = gpu.gptq_quantize_layer(Wd, Ud, bits, group, 128)
+    torch.cuda.synchronize()
+    for name in ("codes", "scales", "zeros", "packed", "row_loss"):
+        assert torch.equal(getattr(qa, name), getattr(qb, name)[:4096]), name
+    rows = np.unique(np.append(np.random.default_rng(94).choice(4096, 48, replace=False), [0, 4095]))
+    check_quant(qa, O.quantize_layer(W[rows], U.astype(np.float64), bits, group, 128, decide=np.float32), bits,
+                rows=rows)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("d_row,d_col", [(1, 1), (3, 10), (7, 11), (5, 128), (9, 1000)])
 def test_pack_parity(gpu, bits, d_row, d_col):
