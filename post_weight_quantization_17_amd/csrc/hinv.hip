@@ -15,17 +15,18 @@
 //
 // L and X = L^-1 are computed together in fp64, 64 columns at a time, with
 // the trailing update applied once per 128-column super-panel S = [s0, s1):
-//   diag  (1 workgroup): A_kk -= L_kS' L_kS'^T over the super-panel's earlier
-//         blocks S' (left-looking), then X_kk = chol(A_kk)^-1; a pivot that
-//         is not positive sets `info`.
-//   panel (many):  row blocks i > k:  L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T,
+//   block (one launch per 64 columns): every workgroup applies
+//         A_kk -= L_kS' L_kS'^T over the super-panel's earlier blocks S'
+//         (left-looking) and factors X_kk = chol(A_kk)^-1 itself (a pivot
+//         that is not positive sets `info`), then computes its tiles of
+//                  row blocks i > k:  L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T,
 //                                     kept column-major in the panel buffer LT
 //                  col blocks c < k:  X_kc = X_kk (R_kc - L_kS' X_S'c)
 //   trail (many, once per super-panel, K = 128):
 //                  A_ij -= L_iS L_jS^T   for i >= j >= s1 (lower tiles)
 //                  R_ic -= L_iS X_Sc     for i >= s1, c < s1
 // R starts as the identity; block row k of R becomes block row k of X once
-// its diag and panel steps have run. All products use the fp64 MFMA
+// its block step has run. All products use the fp64 MFMA
 // (v_mfma_f64_16x16x4f64). The trailing update, which holds almost all of
 // the flops, reads the trailing matrix once per 128 columns instead of once
 // per 64 and keeps 16 independent MFMA chains per wave.
@@ -164,16 +165,29 @@ __device__ __forceinline__ double recip(double x) {
   return r;
 }
 
-// ------------------------------------------------------------ diag block
-// Factor the kb x kb diagonal block at k0, after the left-looking update
-// A_kk -= L_kS' L_kS'^T over the kl earlier columns of the super-panel, and
-// invert its factor.
+// ------------------------------------------------------------ block step
+// One launch per 64-column block k = [k0, k0 + kb) of the super-panel
+// S = [s0, s1), s0 = k0 - kl. Every workgroup first factors the diagonal
+// block itself:
+//   A_kk -= L_kS' L_kS'^T (left-looking over the kl earlier columns of S),
+//   X_kk = chol(A_kk)^-1,
+// with the same instructions on the same data in every workgroup, so every
+// copy of X_kk is the same to the bit. Then it applies X_kk to its own tile:
+//   workgroups [0, nrow): 32 rows i0 = k0 + kb + 32 b of block column k,
+//     L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T, stored column-major in LT
+//     (LT[(kl + m) * d + i] = L[i][k0 + m]);
+//   workgroups [nrow, nrow + ncol): 32 columns c0 = 32 (b - nrow) < k0 of
+//     block row k, X_kc = X_kk (R_kc - L_kS' X_S'c), in place in R.
+// Workgroup 0 also writes X_kk into R's diagonal block and reports a pivot
+// that is not positive. The copies of the 64x64 factorization run side by
+// side, so recomputing it costs the chain nothing, and the block needs one
+// dependent launch instead of two.
 //
-// Gauss-Jordan form on one symmetric 64x64 array v: step j eliminates
-// column j with multipliers m_i = v_ij / v_jj (i > j). Columns c > j still
-// hold the Schur complement (v_ic -= m_i v_jc); columns c < j hold the
-// unit-lower inverse Y (v_ic -= m_i y_jc); column j itself becomes Y's
-// column j (-m_i, and 1 on the diagonal). Row j of v therefore carries
+// The factorization is Gauss-Jordan on one symmetric 64x64 array v: step j
+// eliminates column j with multipliers m_i = v_ij / v_jj (i > j). Columns
+// c > j still hold the Schur complement (v_ic -= m_i v_jc); columns c < j
+// hold the unit-lower inverse Y (v_ic -= m_i y_jc); column j itself becomes
+// Y's column j (-m_i, and 1 on the diagonal). Row j of v therefore carries
 // everything step j needs: y_jc left of the diagonal, the pivot, and the
 // Schur row, which equals the Schur column by symmetry (m_i = v_ji / v_jj).
 // After 64 steps X_kk = L^-1 has X_ic = y_ic / sqrt(pivot_i). Rows and
@@ -183,44 +197,25 @@ __device__ __forceinline__ double recip(double x) {
 // registers for all 64 steps; the 16 threads that hold rows j and j+1 (one
 // quarter of one wave) write them to LDS, double buffered, one barrier per
 // two steps.
-__global__ void __launch_bounds__(256)
-hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, int k0, int kb,
-          int kl, double* __restrict__ Xkk, double* __restrict__ XkkT, int32_t* __restrict__ info) {
-  __shared__ double Ls[KS - NB][NB + 4];  // Ls[m][i] = L[k0 + i][s0 + m]
-  __shared__ double T[NB][NB + 1];
-  __shared__ __attribute__((aligned(16))) double bv[2][2][NB];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  // issue every load first: the diagonal block and the panel rows L_kS'
-  constexpr int PER = NB * NB / 256;
-  double av[PER], lv[PER];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
-    const bool ok = i < kb && j <= i;
-    av[t] = A[ok ? int64_t(k0 + i) * d + k0 + j : int64_t(k0) * d + k0];
-    const int m = e >> 6, c = e & 63;  // m < kl, c < 64
-    const bool lok = m < kl;
-    lv[t] = LT[lok ? int64_t(m) * d + k0 + (c < kb ? c : kb - 1) : 0];
-  }
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
-    T[i][j] = (i < kb && j <= i) ? av[t] : 0.0;
-    if ((e >> 6) < kl) Ls[e >> 6][e & 63] = lv[t];
-  }
-  __syncthreads();
-  if (kl > 0) {
-    // wave w: rows 16 w .. + 16, all four column blocks
-    doublex4 acc[4];
-    zero(acc);
-    const int ri[4] = {16 * wave, 16 * wave, 16 * wave, 16 * wave};
-    const int cj[4] = {0, 16, 32, 48};
-    blocks_mma<4, true>(acc, &Ls[0][0], NB + 4, &Ls[0][0], NB + 4, ri, cj, kl);
-    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { T[i][j] -= s; });
-    __syncthreads();
-  }
+constexpr int PP = NB + 4;  // LDS pitch (doubles) of 64-wide tiles
+constexpr int PQ = 32 + 4;  // LDS pitch of 32-wide tiles
+// Workgroups of one block step. Each factors the diagonal block itself, so
+// more workgroups take CU time from the trailing update running beside
+// them; beyond this count a workgroup takes several tiles.
+constexpr int BLOCK_MAX_WG = 128;
+
+// v <- the factorization of the block whose lower part is in T (T[i][j],
+// j <= i < kb); dr <- the pivots of the thread's rows. Two steps per
+// barrier: the owners of rows j and j+1 (j even) publish both rows; every
+// thread applies step j, derives row j+1 after step j at the positions it
+// needs (its 4 rows, its 4 columns, the pivot pair) with the same
+// arithmetic the owners use, and applies step j+1. A loop of 16 iterations
+// of 4 unrolled steps keeps the body small enough to run from the
+// instruction cache (each launch runs it once).
+__device__ __forceinline__ void diag_factor(const double (*T)[PP], int kb, double (&v)[4][4], double (&dr)[4],
+                                            double (*bv)[2][NB]) {
+  const int tid = threadIdx.x;
   const int rb_ = 4 * (tid >> 4), cb_ = 4 * (tid & 15);
-  double v[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -230,13 +225,8 @@ hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __
       const double t = T[i > j ? i : j][i > j ? j : i];
       v[r][c] = in ? t : (i == j ? 1.0 : 0.0);
     }
-  double dr[4] = {1.0, 1.0, 1.0, 1.0};
-  // Two steps per barrier: the owners of rows j and j+1 (j even) publish
-  // both rows; every thread applies step j, derives row j+1 after step j at
-  // the positions it needs (its 4 rows, its 4 columns, the pivot pair) with
-  // the same arithmetic the owners use, and applies step j+1. A loop of 16
-  // iterations of 4 unrolled steps keeps the body small enough to run from
-  // the instruction cache (each launch runs it once).
+#pragma unroll
+  for (int r = 0; r < 4; ++r) dr[r] = 1.0;
 #pragma nounroll
   for (int jb = 0; jb < NB; jb += 4) {
     static_for<0, 2>([&](auto hc) {
@@ -313,21 +303,177 @@ hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __
         }
     });
   }
-  // The first pivot that is not positive (NaN included) sets `info` to one
-  // plus its index in H.
-  __shared__ int bad;
-  if (tid == 0) bad = NB;
-  __syncthreads();
-  if (cb_ == 0) {
+}
+
+// A workgroup's panel tile: rows i0 = k0 + kb + 32 tb (tb < nrow) or
+// columns c0 = 32 (tb - nrow) (otherwise). Its operands: lo = L_iS' (row
+// tile) or X_S'c (column tile), 32 x kl; cv = A_ik (32 x kb) or R_kc
+// (kb x 32).
+struct BlockArgs {
+  const double* A;
+  double* R;
+  double* LT;
+  int d, k0, kb, kl, nrow, ntile;
+};
+
+__device__ __forceinline__ void tile_load(const BlockArgs& g, int tb, double (&lo)[8], double (&cv)[8]) {
+  const int tid = threadIdx.x, d = g.d;
+  const bool rowpart = tb < g.nrow;
+  const int i0 = g.k0 + g.kb + 32 * tb, c0 = 32 * (tb - g.nrow), s0 = g.k0 - g.kl;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (rb_ + r < kb && !(dr[r] > 0.0)) atomicMin(&bad, rb_ + r);
+  for (int t = 0; t < 8; ++t) {
+    const int e = tid + 256 * t;
+    if (rowpart) {
+      const int m = e >> 5, i = e & 31;
+      const int gi = i0 + i < d ? i0 + i : d - 1;
+      lo[t] = g.LT[m < g.kl ? int64_t(m) * d + gi : 0];
+      const int ii = e >> 6, mm = e & 63;  // C source: A[i0 + ii][k0 + mm]
+      const bool ok = i0 + ii < d && mm < g.kb;
+      cv[t] = g.A[ok ? int64_t(i0 + ii) * d + g.k0 + mm : 0];
+      cv[t] = ok ? cv[t] : 0.0;
+    } else {
+      const int m = e >> 5, c = e & 31;
+      lo[t] = g.R[m < g.kl ? int64_t(s0 + m) * d + c0 + c : 0];
+      const int ii = e >> 5, cc = e & 31;  // C source: R[k0 + ii][c0 + cc]
+      const bool ok = ii < g.kb;
+      cv[t] = g.R[ok ? int64_t(g.k0 + ii) * d + c0 + cc : 0];
+      cv[t] = ok ? cv[t] : 0.0;
+    }
   }
+}
+
+// Lo[m][i] (row tile) or Lo[m][c] (column tile); C[i][m] at Cs[i * PP + m]
+// (row tile, 32 x 64) or C[i][c] at Cs[i * PQ + c] (column tile, 64 x 32).
+__device__ __forceinline__ void tile_stage(bool rowpart, const double (&lo)[8], const double (&cv)[8],
+                                           double (*Lo)[PQ], double* Cs) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int e = tid + 256 * t;
+    Lo[e >> 5][e & 31] = lo[t];
+    Cs[rowpart ? (e >> 6) * PP + (e & 63) : (e >> 5) * PQ + (e & 31)] = cv[t];
+  }
+}
+
+// C -= L_iS' L_kS'^T (row tile) or C -= L_kS' X_S'c (column tile), K = kl.
+__device__ __forceinline__ void tile_update(bool rowpart, int kl, const double (*Lk)[PP], const double (*Lo)[PQ],
+                                            double* Cs) {
+  const int wave = threadIdx.x >> 6;
+  doublex4 acc[2];
+  zero(acc);
+  if (rowpart) {
+    const int ri[2] = {0, 16};
+    const int cj[2] = {16 * wave, 16 * wave};
+    blocks_mma<2, true>(acc, &Lo[0][0], PQ, &Lk[0][0], PP, ri, cj, kl);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PP + j] -= s; });
+  } else {
+    const int ri[2] = {16 * wave, 16 * wave};
+    const int cj[2] = {0, 16};
+    blocks_mma<2, true>(acc, &Lk[0][0], PP, &Lo[0][0], PQ, ri, cj, kl);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PQ + j] -= s; });
+  }
+}
+
+// The tile's output, from X_kk^T in XT: L_ik = C X_kk^T, transposed
+// through Lo into coalesced column-major stores in LT (row tile), or
+// X_kc = X_kk C written in place into R (column tile).
+__device__ __forceinline__ void tile_product(const BlockArgs& g, int tb, const double (*XT)[PP], const double* Cs,
+                                             double (*Lo)[PQ]) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int Kp = (g.kb + 3) & ~3;
+  doublex4 acc[2];
+  zero(acc);
+  if (tb < g.nrow) {
+    // output 32 x 64: wave w owns rows 0..31 of column block w
+    const int i0 = g.k0 + g.kb + 32 * tb;
+    const int ri[2] = {0, 16};
+    const int cj[2] = {16 * wave, 16 * wave};
+    blocks_mma<2, false>(acc, Cs, PP, &XT[0][0], PP, ri, cj, Kp);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lo[j][i] = s; });
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int e = tid + 256 * t, m = e >> 5, i = e & 31;
+      if (m < g.kb && i0 + i < g.d) g.LT[int64_t(g.kl + m) * g.d + i0 + i] = Lo[m][i];
+    }
+  } else {
+    // output 64 x 32: wave w owns row block w, both column blocks; the A
+    // operand X_kk[i][m] is read k-major from X_kk^T
+    const int c0 = 32 * (tb - g.nrow);
+    const int ri[2] = {16 * wave, 16 * wave};
+    const int cj[2] = {0, 16};
+    blocks_mma<2, true>(acc, &XT[0][0], PP, Cs, PQ, ri, cj, Kp);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
+      if (i < g.kb) g.R[int64_t(g.k0 + i) * g.d + c0 + j] = s;
+    });
+  }
+}
+
+// Grid: min(ntile, BLOCK_MAX_WG) workgroups (at least 1); workgroup b takes
+// tiles b, b + grid, ... The first tile's operands are loaded and its update
+// applied together with the diagonal block's, before the factorization.
+__global__ void __launch_bounds__(256)
+hinv_block(const BlockArgs g, int32_t* __restrict__ info) {
+  __shared__ double Lk[NB][PP];   // Lk[m][i] = L[k0 + i][s0 + m]
+  __shared__ double Xs[NB][PP];   // A_kk (lower part) during the factorization, then X_kk^T
+  __shared__ double Lo[NB][PQ];   // the tile's L_iS' or X_S'c; then the transposed row-tile output
+  __shared__ double Cs[NB * PQ];  // the tile's C
+  __shared__ __attribute__((aligned(16))) double bv[2][2][NB];
+  __shared__ int bad;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int bid = int(blockIdx.x);
+  const int d = g.d, k0 = g.k0, kb = g.kb, kl = g.kl;
+  // every load first: the diagonal block, the panel rows L_kS', and the
+  // first tile's operands
+  constexpr int PER = NB * NB / 256;
+  double av[PER], lk[PER], lo[8], cv[8];
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
+    const bool ok = i < kb && j <= i;
+    av[t] = g.A[ok ? int64_t(k0 + i) * d + k0 + j : int64_t(k0) * d + k0];
+    lk[t] = g.LT[i < kl ? int64_t(i) * d + k0 + (j < kb ? j : kb - 1) : 0];  // i = m, j = column in the block
+  }
+  const bool first = bid < g.ntile;
+  if (first) tile_load(g, bid, lo, cv);
+#pragma unroll
+  for (int t = 0; t < PER; ++t) {
+    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
+    Xs[i][j] = (i < kb && j <= i) ? av[t] : 0.0;
+    Lk[i][j] = lk[t];
+  }
+  if (first) tile_stage(bid < g.nrow, lo, cv, Lo, Cs);
   __syncthreads();
-  if (tid == 0 && bad < NB) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + bad)));
-  // X_kk = D^-1/2 Y, staged in LDS (T is free again) and written row-major
-  // and transposed for the panel step, and into R's diagonal block (zeros
-  // above the diagonal), all as coalesced rows.
+  if (kl > 0) {
+    // the diagonal block: wave w, rows 16 w .. + 16, all four column blocks
+    doublex4 acc[4];
+    zero(acc);
+    const int ri[4] = {16 * wave, 16 * wave, 16 * wave, 16 * wave};
+    const int cj[4] = {0, 16, 32, 48};
+    blocks_mma<4, true>(acc, &Lk[0][0], PP, &Lk[0][0], PP, ri, cj, kl);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Xs[i][j] -= s; });
+    if (first) tile_update(bid < g.nrow, kl, Lk, Lo, Cs);
+    __syncthreads();
+  }
+  double v[4][4], dr[4];
+  diag_factor(Xs, kb, v, dr, bv);  // reads Xs before its first barrier
+  const int rb_ = 4 * (tid >> 4), cb_ = 4 * (tid & 15);
+  if (bid == 0) {
+    // The first pivot that is not positive (NaN included) sets `info` to one
+    // plus its index in H.
+    if (tid == 0) bad = NB;
+    __syncthreads();
+    if (cb_ == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (rb_ + r < kb && !(dr[r] > 0.0)) atomicMin(&bad, rb_ + r);
+    }
+    __syncthreads();
+    if (tid == 0 && bad < NB) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + bad)));
+  }
+  // X_kk = D^-1/2 Y (zero above the diagonal and past kb), stored
+  // transposed in Xs; workgroup 0 also writes it into R's diagonal block.
+  // Every thread has read Xs in diag_factor before its first barrier.
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = rb_ + r;
@@ -335,125 +481,24 @@ hinv_diag(const double* __restrict__ A, double* __restrict__ R, const double* __
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int j = cb_ + c;
-      T[i][j] = (i < kb && j <= i) ? v[r][c] * si : 0.0;
+      const double x = (i < kb && j <= i) ? v[r][c] * si : 0.0;
+      Xs[j][i] = x;
+      if (bid == 0 && i < kb && j < kb) g.R[int64_t(k0 + i) * d + k0 + j] = x;
     }
   }
   __syncthreads();
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
-    const double x = T[i][j];
-    Xkk[e] = x;
-    XkkT[e] = T[j][i];
-    if (i < kb && j < kb) R[int64_t(k0 + i) * d + k0 + j] = x;
-  }
-}
-
-// ------------------------------------------------------------ panel step
-// Blocks [0, nrow): 32 rows i0 = k0 + kb + 32 b .. of block column k:
-//   L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T, stored column-major in LT
-//   (LT[(kl + m) * d + i] = L[i][k0 + m]).
-// Blocks [nrow, nrow + ncol): 32 columns c0 = 32 (b - nrow) < k0 of block
-// row k:  X_kc = X_kk (R_kc - L_kS' X_S'c), in place in R.
-// S' = [k0 - kl, k0) are the super-panel's earlier columns (kl <= 64).
-// Every operand load is issued before the first product.
-constexpr int PP = NB + 4;  // LDS pitch (doubles) of 64-wide panel tiles
-constexpr int PQ = 32 + 4;  // LDS pitch of 32-wide panel tiles
-__global__ void __launch_bounds__(256)
-hinv_panel(const double* __restrict__ A, double* __restrict__ R, double* __restrict__ LT, int d, int k0, int kb,
-           int kl, const double* __restrict__ Xkk, const double* __restrict__ XkkT, int nrow) {
-  __shared__ double Lk[NB][PP];   // Lk[m][i] = L[k0 + i][s0 + m]
-  __shared__ double Xs[NB][PP];   // X_kk^T (row part) or X_kk (column part)
-  __shared__ double Lo[NB][PQ];   // row part: L[i0 + i][s0 + m] as Lo[m][i]; column part: X_S'c as Lo[m][c]
-  __shared__ double Cs[NB][PP];   // row part: C[i][m] (32 x 64); column part: C[i][c] (64 x 32)
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int s0 = k0 - kl;
-  const int Kp = (kb + 3) & ~3;
-  const bool rowpart = int(blockIdx.x) < nrow;
-  const int i0 = k0 + kb + 32 * blockIdx.x;           // row part
-  const int c0 = 32 * (int(blockIdx.x) - nrow);       // column part
-  double lk[16], x[16], lo[8], cv[8];
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int e = tid + 256 * t, m = e >> 6, c = e & 63;
-    lk[t] = LT[m < kl ? int64_t(m) * d + k0 + (c < kb ? c : kb - 1) : 0];
-    x[t] = rowpart ? XkkT[e] : Xkk[e];
-  }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int e = tid + 256 * t;
-    if (rowpart) {
-      const int m = e >> 5, i = e & 31;
-      const int gi = i0 + i < d ? i0 + i : d - 1;
-      lo[t] = LT[m < kl ? int64_t(m) * d + gi : 0];
-      const int ii = e >> 6, mm = e & 63;  // C source: A[i0 + ii][k0 + mm]
-      const bool ok = i0 + ii < d && mm < kb;
-      cv[t] = A[ok ? int64_t(i0 + ii) * d + k0 + mm : 0];
-      cv[t] = ok ? cv[t] : 0.0;
-    } else {
-      const int m = e >> 5, c = e & 31;
-      lo[t] = R[m < kl ? int64_t(s0 + m) * d + c0 + c : 0];
-      const int ii = e >> 5, cc = e & 31;  // C source: R[k0 + ii][c0 + cc]
-      const bool ok = ii < kb;
-      cv[t] = R[ok ? int64_t(k0 + ii) * d + c0 + cc : 0];
-      cv[t] = ok ? cv[t] : 0.0;
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int e = tid + 256 * t;
-    Lk[e >> 6][e & 63] = lk[t];
-    Xs[e >> 6][e & 63] = x[t];
-  }
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int e = tid + 256 * t;
-    Lo[e >> 5][e & 31] = lo[t];
-    if (rowpart)
-      Cs[e >> 6][e & 63] = cv[t];
-    else
-      Cs[e >> 5][e & 31] = cv[t];
-  }
-  __syncthreads();
-  if (rowpart) {
-    // output 32 x 64: wave w owns rows 0..31 of column block w
-    const int ri[2] = {0, 16};
-    const int cj[2] = {16 * wave, 16 * wave};
-    doublex4 acc[2];
-    if (kl > 0) {
-      zero(acc);
-      blocks_mma<2, true>(acc, &Lo[0][0], PQ, &Lk[0][0], PP, ri, cj, kl);
-      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i][j] -= s; });
+  for (int tb = bid; tb < g.ntile; tb += int(gridDim.x)) {
+    if (tb != bid) {
+      tile_load(g, tb, lo, cv);
+      __syncthreads();  // the previous tile is done with Lo and Cs
+      tile_stage(tb < g.nrow, lo, cv, Lo, Cs);
       __syncthreads();
+      if (kl > 0) {
+        tile_update(tb < g.nrow, kl, Lk, Lo, Cs);
+        __syncthreads();
+      }
     }
-    zero(acc);
-    blocks_mma<2, false>(acc, &Cs[0][0], PP, &Xs[0][0], PP, ri, cj, Kp);
-    // transpose through LDS (Lo is free again), then coalesced stores
-    __syncthreads();
-    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lk[j][i] = s; });
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int e = tid + 256 * t, m = e >> 5, i = e & 31;
-      if (m < kb && i0 + i < d) LT[int64_t(kl + m) * d + i0 + i] = Lk[m][i];
-    }
-  } else {
-    // output 64 x 32: wave w owns row block w, both column blocks
-    const int ri[2] = {16 * wave, 16 * wave};
-    const int cj[2] = {0, 16};
-    doublex4 acc[2];
-    if (kl > 0) {
-      zero(acc);
-      blocks_mma<2, true>(acc, &Lk[0][0], PP, &Lo[0][0], PQ, ri, cj, kl);
-      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i][j] -= s; });
-      __syncthreads();
-    }
-    zero(acc);
-    // X_kc = X_kk C: A operand X_kk[i][m] row-major in Xs, B operand C[m][c]
-    blocks_mma<2, false>(acc, &Xs[0][0], PP, &Cs[0][0], PP, ri, cj, Kp);
-    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
-      if (i < kb) R[int64_t(k0 + i) * d + c0 + j] = s;
-    });
+    tile_product(g, tb, Xs, Cs, Lo);
   }
 }
 
@@ -605,7 +650,7 @@ hinv_write_u(const double* __restrict__ R, int d, float* __restrict__ U) {
 }
 
 struct HinvWs {
-  double *A, *R, *LT, *lam, *Xkk, *XkkT;
+  double *A, *R, *LT, *lam;
   size_t bytes;
 };
 
@@ -613,15 +658,12 @@ HinvWs carve(void* ws, int64_t d) {
   HinvWs w{};
   const size_t mat = align_up(size_t(d) * d * sizeof(double), 256);
   const size_t panel = align_up(size_t(2) * KS * d * sizeof(double), 256);  // double buffered
-  const size_t blk = align_up(NB * NB * sizeof(double), 256);
   char* p = static_cast<char*>(ws);
   w.A = reinterpret_cast<double*>(p);
   w.R = reinterpret_cast<double*>(p + mat);
   w.LT = reinterpret_cast<double*>(p + 2 * mat);
   w.lam = reinterpret_cast<double*>(p + 2 * mat + panel);
-  w.Xkk = reinterpret_cast<double*>(p + 2 * mat + panel + 256);
-  w.XkkT = reinterpret_cast<double*>(p + 2 * mat + panel + 256 + blk);
-  w.bytes = 2 * mat + panel + 256 + 2 * blk;
+  w.bytes = 2 * mat + panel + 256;
   return w;
 }
 
@@ -682,7 +724,7 @@ extern "C" size_t gptq_prepare_hinv_workspace_size(int64_t d) {
 
 // Schedule (S = the caller's stream, X = the auxiliary stream). For each
 // super-panel p = [s0, s1), with s2 = s1 + KS:
-//   S: diag/panel steps of p (writing the panel buffer LT[p % 2])
+//   S: the block steps of p (writing the panel buffer LT[p % 2])
 //   S: wait for X's trailing update of p - 1, then apply p to the next
 //      super-panel's columns [s1, s2) and R rows [s1, s2)   ("trail A")
 //   X: after trail A, apply p to everything at and beyond s2 ("trail B"),
@@ -718,12 +760,11 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     for (int k0 = s0; k0 < s1; k0 += NB) {
       const int kb = s1 - k0 < NB ? s1 - k0 : NB;
       const int kl = k0 - s0;
-      hipLaunchKernelGGL(hinv_diag, dim3(1), dim3(256), 0, s, w.A, w.R, LTp, di, k0, kb, kl, w.Xkk, w.XkkT, info);
       const int nrow = (di - k0 - kb + 31) / 32;
-      const int ncol = k0 / 32;
-      if (nrow + ncol > 0)
-        hipLaunchKernelGGL(hinv_panel, dim3(unsigned(nrow + ncol)), dim3(256), 0, s, w.A, w.R, LTw, di, k0, kb, kl,
-                           w.Xkk, w.XkkT, nrow);
+      const int ntile = nrow + k0 / 32;
+      const int grid = ntile < 1 ? 1 : (ntile < BLOCK_MAX_WG ? ntile : BLOCK_MAX_WG);
+      const BlockArgs args{w.A, w.R, LTw, di, k0, kb, kl, nrow, ntile};
+      hipLaunchKernelGGL(hinv_block, dim3(unsigned(grid)), dim3(256), 0, s, args, info);
     }
     if (s1 < di) {
       const int s2 = di - s1 < KS ? di : s1 + KS;
