@@ -165,23 +165,28 @@ __device__ __forceinline__ double recip(double x) {
   return r;
 }
 
-// ------------------------------------------------------------ block step
-// One launch per 64-column block k = [k0, k0 + kb) of the super-panel
-// S = [s0, s1), s0 = k0 - kl. Every workgroup first factors the diagonal
-// block itself:
-//   A_kk -= L_kS' L_kS'^T (left-looking over the kl earlier columns of S),
-//   X_kk = chol(A_kk)^-1,
-// with the same instructions on the same data in every workgroup, so every
-// copy of X_kk is the same to the bit. Then it applies X_kk to its own tile:
-//   workgroups [0, nrow): 32 rows i0 = k0 + kb + 32 b of block column k,
-//     L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T, stored column-major in LT
-//     (LT[(kl + m) * d + i] = L[i][k0 + m]);
-//   workgroups [nrow, nrow + ncol): 32 columns c0 = 32 (b - nrow) < k0 of
-//     block row k, X_kc = X_kk (R_kc - L_kS' X_S'c), in place in R.
-// Workgroup 0 also writes X_kk into R's diagonal block and reports a pivot
-// that is not positive. The copies of the 64x64 factorization run side by
-// side, so recomputing it costs the chain nothing, and the block needs one
-// dependent launch instead of two.
+// ------------------------------------------------------------ super-panel step
+// One launch per super-panel S = [s0, s1): block k0 = s0 (kb0 <= 64
+// columns) and, when S is wider than 64, block k1 = s0 + 64 (kb1 <= 64
+// columns; kb0 = 64 then). Every workgroup computes, with the same
+// instructions on the same data, so that every copy is the same to the bit:
+//   X_k0 = chol(A_k0k0)^-1,
+//   L_k1k0 = A_k1k0 X_k0^T,
+//   X_k1 = chol(A_k1k1 - L_k1k0 L_k1k0^T)^-1,
+// and then its own tiles of both blocks:
+//   rows i >= s1 (32 at a time):  L_ik0 = A_ik0 X_k0^T,
+//                                 L_ik1 = (A_ik1 - L_ik0 L_k1k0^T) X_k1^T,
+//                                 both column-major in the panel buffer LT
+//                                 (LT[m * d + i] = L[i][s0 + m]);
+//   columns c < s0 (32 at a time): X_k0c = X_k0 R_k0c,
+//                                 X_k1c = X_k1 (R_k1c - L_k1k0 X_k0c), in R;
+//   columns c in [s0, s0 + 64):   X_k1c = X_k1 (R_k1c - L_k1k0 X_k0c), with
+//                                 X_k0c taken from X_k0 itself.
+// Workgroup 0 also writes X_k0 and X_k1 into R's diagonal blocks and
+// reports a pivot that is not positive. The copies of the two 64x64
+// factorizations run side by side, so recomputing them costs the chain
+// nothing: the super-panel needs one dependent launch, and the second
+// block does not wait for the first block's panel to reach memory.
 //
 // The factorization is Gauss-Jordan on one symmetric 64x64 array v: step j
 // eliminates column j with multipliers m_i = v_ij / v_jj (i > j). Columns
@@ -199,10 +204,10 @@ __device__ __forceinline__ double recip(double x) {
 // two steps.
 constexpr int PP = NB + 4;  // LDS pitch (doubles) of 64-wide tiles
 constexpr int PQ = 32 + 4;  // LDS pitch of 32-wide tiles
-// Workgroups of one block step. Each factors the diagonal block itself, so
-// more workgroups take CU time from the trailing update running beside
-// them; beyond this count a workgroup takes several tiles.
-constexpr int BLOCK_MAX_WG = 128;
+// Workgroups of one super-panel step. Each factors the diagonal blocks
+// itself, so more workgroups take CU time from the trailing update running
+// beside them; beyond this count a workgroup takes several tiles.
+constexpr int STEP_MAX_WG = 128;
 
 // v <- the factorization of the block whose lower part is in T (T[i][j],
 // j <= i < kb); dr <- the pivots of the thread's rows. Two steps per
@@ -305,175 +310,165 @@ __device__ __forceinline__ void diag_factor(const double (*T)[PP], int kb, doubl
   }
 }
 
-// A workgroup's panel tile: rows i0 = k0 + kb + 32 tb (tb < nrow) or
-// columns c0 = 32 (tb - nrow) (otherwise). Its operands: lo = L_iS' (row
-// tile) or X_S'c (column tile), 32 x kl; cv = A_ik (32 x kb) or R_kc
-// (kb x 32).
-struct BlockArgs {
+struct StepArgs {
   const double* A;
   double* R;
   double* LT;
-  int d, k0, kb, kl, nrow, ntile;
+  int d, k0, kb0, kb1;
+  int nrow, ncol, ntile;  // nrow row tiles, ncol column tiles below s0, then 2 more when kb1 > 0
 };
 
-__device__ __forceinline__ void tile_load(const BlockArgs& g, int tb, double (&lo)[8], double (&cv)[8]) {
-  const int tid = threadIdx.x, d = g.d;
-  const bool rowpart = tb < g.nrow;
-  const int i0 = g.k0 + g.kb + 32 * tb, c0 = 32 * (tb - g.nrow), s0 = g.k0 - g.kl;
+// The tile's operands for block k0 (A_ik0 or R_k0c; nothing for the two
+// column tiles inside the first block) and for block k1 (A_ik1 or R_k1c).
+__device__ __forceinline__ void step_load(const StepArgs& g, int tb, double (&c0v)[8], double (&c1v)[8]) {
+  const int tid = threadIdx.x, d = g.d, k1 = g.k0 + NB;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int e = tid + 256 * t;
-    if (rowpart) {
-      const int m = e >> 5, i = e & 31;
-      const int gi = i0 + i < d ? i0 + i : d - 1;
-      lo[t] = g.LT[m < g.kl ? int64_t(m) * d + gi : 0];
-      const int ii = e >> 6, mm = e & 63;  // C source: A[i0 + ii][k0 + mm]
-      const bool ok = i0 + ii < d && mm < g.kb;
-      cv[t] = g.A[ok ? int64_t(i0 + ii) * d + g.k0 + mm : 0];
-      cv[t] = ok ? cv[t] : 0.0;
+    if (tb < g.nrow) {
+      const int i0 = g.k0 + g.kb0 + g.kb1 + 32 * tb;
+      const int ii = e >> 6, mm = e & 63;  // A[i0 + ii][k0 + mm], A[i0 + ii][k1 + mm]
+      const bool ok0 = i0 + ii < d && mm < g.kb0;
+      const bool ok1 = i0 + ii < d && mm < g.kb1;
+      c0v[t] = g.A[ok0 ? int64_t(i0 + ii) * d + g.k0 + mm : 0];
+      c0v[t] = ok0 ? c0v[t] : 0.0;
+      c1v[t] = g.A[ok1 ? int64_t(i0 + ii) * d + k1 + mm : 0];
+      c1v[t] = ok1 ? c1v[t] : 0.0;
     } else {
-      const int m = e >> 5, c = e & 31;
-      lo[t] = g.R[m < g.kl ? int64_t(s0 + m) * d + c0 + c : 0];
-      const int ii = e >> 5, cc = e & 31;  // C source: R[k0 + ii][c0 + cc]
-      const bool ok = ii < g.kb;
-      cv[t] = g.R[ok ? int64_t(g.k0 + ii) * d + c0 + cc : 0];
-      cv[t] = ok ? cv[t] : 0.0;
+      const int c0 = 32 * (tb - g.nrow);
+      const int ii = e >> 5, cc = e & 31;  // R[k0 + ii][c0 + cc], R[k1 + ii][c0 + cc]
+      const bool ok0 = tb < g.nrow + g.ncol && ii < g.kb0;
+      const bool ok1 = ii < g.kb1;
+      c0v[t] = g.R[ok0 ? int64_t(g.k0 + ii) * d + c0 + cc : 0];
+      c0v[t] = ok0 ? c0v[t] : 0.0;
+      c1v[t] = g.R[ok1 ? int64_t(k1 + ii) * d + c0 + cc : 0];
+      c1v[t] = ok1 ? c1v[t] : 0.0;
     }
   }
 }
 
-// Lo[m][i] (row tile) or Lo[m][c] (column tile); C[i][m] at Cs[i * PP + m]
-// (row tile, 32 x 64) or C[i][c] at Cs[i * PQ + c] (column tile, 64 x 32).
-__device__ __forceinline__ void tile_stage(bool rowpart, const double (&lo)[8], const double (&cv)[8],
-                                           double (*Lo)[PQ], double* Cs) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int e = tid + 256 * t;
-    Lo[e >> 5][e & 31] = lo[t];
-    Cs[rowpart ? (e >> 6) * PP + (e & 63) : (e >> 5) * PQ + (e & 31)] = cv[t];
-  }
-}
-
-// C -= L_iS' L_kS'^T (row tile) or C -= L_kS' X_S'c (column tile), K = kl.
-__device__ __forceinline__ void tile_update(bool rowpart, int kl, const double (*Lk)[PP], const double (*Lo)[PQ],
-                                            double* Cs) {
-  const int wave = threadIdx.x >> 6;
+// One tile of both blocks, its operands in c0v / c1v. XT0, XT1 hold
+// X_k0^T, X_k1^T; Lk[m][i] = L[k1 + i][k0 + m]. Begins after a barrier and
+// ends with one.
+__device__ __forceinline__ void step_tile(const StepArgs& g, int tb, const double (&c0v)[8], const double (&c1v)[8],
+                                          const double (*XT0)[PP], const double (*XT1)[PP], const double (*Lk)[PP],
+                                          double (*Lo)[PQ], double* Cs) {
+  const int tid = threadIdx.x, wave = tid >> 6, d = g.d, k1 = g.k0 + NB;
+  const int Kp0 = (g.kb0 + 3) & ~3, Kp1 = (g.kb1 + 3) & ~3;
+  const bool two = g.kb1 > 0;
   doublex4 acc[2];
-  zero(acc);
-  if (rowpart) {
-    const int ri[2] = {0, 16};
-    const int cj[2] = {16 * wave, 16 * wave};
-    blocks_mma<2, true>(acc, &Lo[0][0], PQ, &Lk[0][0], PP, ri, cj, kl);
-    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PP + j] -= s; });
-  } else {
-    const int ri[2] = {16 * wave, 16 * wave};
-    const int cj[2] = {0, 16};
-    blocks_mma<2, true>(acc, &Lk[0][0], PP, &Lo[0][0], PQ, ri, cj, kl);
-    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PQ + j] -= s; });
-  }
-}
-
-// The tile's output, from X_kk^T in XT: L_ik = C X_kk^T, transposed
-// through Lo into coalesced column-major stores in LT (row tile), or
-// X_kc = X_kk C written in place into R (column tile).
-__device__ __forceinline__ void tile_product(const BlockArgs& g, int tb, const double (*XT)[PP], const double* Cs,
-                                             double (*Lo)[PQ]) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int Kp = (g.kb + 3) & ~3;
-  doublex4 acc[2];
-  zero(acc);
   if (tb < g.nrow) {
-    // output 32 x 64: wave w owns rows 0..31 of column block w
-    const int i0 = g.k0 + g.kb + 32 * tb;
+    // output 32 x 64 per block: wave w owns rows 0..31 of column block w
+    const int i0 = g.k0 + g.kb0 + g.kb1 + 32 * tb;
     const int ri[2] = {0, 16};
     const int cj[2] = {16 * wave, 16 * wave};
-    blocks_mma<2, false>(acc, Cs, PP, &XT[0][0], PP, ri, cj, Kp);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int e = tid + 256 * t;
+      Cs[(e >> 6) * PP + (e & 63)] = c0v[t];  // A_ik0
+    }
+    __syncthreads();
+    zero(acc);
+    blocks_mma<2, false>(acc, Cs, PP, &XT0[0][0], PP, ri, cj, Kp0);
+    // transpose through LDS, then coalesced stores: Lo[m][i] = L_ik0
     blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lo[j][i] = s; });
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int e = tid + 256 * t, m = e >> 5, i = e & 31;
-      if (m < g.kb && i0 + i < g.d) g.LT[int64_t(g.kl + m) * g.d + i0 + i] = Lo[m][i];
+      if (m < g.kb0 && i0 + i < d) g.LT[int64_t(m) * d + i0 + i] = Lo[m][i];
+    }
+    if (two) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = tid + 256 * t;
+        Cs[(e >> 6) * PP + (e & 63)] = c1v[t];  // A_ik1
+      }
+      __syncthreads();
+      zero(acc);
+      blocks_mma<2, true>(acc, &Lo[0][0], PQ, &Lk[0][0], PP, ri, cj, NB);
+      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PP + j] -= s; });
+      __syncthreads();
+      zero(acc);
+      blocks_mma<2, false>(acc, Cs, PP, &XT1[0][0], PP, ri, cj, Kp1);
+      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lo[j][i] = s; });  // L_ik1
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = tid + 256 * t, m = e >> 5, i = e & 31;
+        if (m < g.kb1 && i0 + i < d) g.LT[int64_t(NB + m) * d + i0 + i] = Lo[m][i];
+      }
     }
   } else {
-    // output 64 x 32: wave w owns row block w, both column blocks; the A
-    // operand X_kk[i][m] is read k-major from X_kk^T
+    // output 64 x 32 per block: wave w owns row block w, both column blocks
     const int c0 = 32 * (tb - g.nrow);
     const int ri[2] = {16 * wave, 16 * wave};
     const int cj[2] = {0, 16};
-    blocks_mma<2, true>(acc, &XT[0][0], PP, Cs, PQ, ri, cj, Kp);
-    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
-      if (i < g.kb) g.R[int64_t(g.k0 + i) * g.d + c0 + j] = s;
-    });
+    if (tb < g.nrow + g.ncol) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = tid + 256 * t;
+        Cs[(e >> 5) * PQ + (e & 31)] = c0v[t];  // R_k0c
+      }
+      __syncthreads();
+      // X_k0c = X_k0 C, the A operand X_k0[i][m] read k-major from X_k0^T
+      zero(acc);
+      blocks_mma<2, true>(acc, &XT0[0][0], PP, Cs, PQ, ri, cj, Kp0);
+      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
+        Lo[i][j] = s;
+        if (i < g.kb0) g.R[int64_t(g.k0 + i) * d + c0 + j] = s;
+      });
+    } else {
+      // inside the first block: X_k0c is X_k0 itself (zero above its diagonal)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = tid + 256 * t, m = e >> 5, c = e & 31;
+        Lo[m][c] = XT0[c0 - g.k0 + c][m];
+      }
+    }
+    if (two) {
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = tid + 256 * t;
+        Cs[(e >> 5) * PQ + (e & 31)] = c1v[t];  // R_k1c
+      }
+      __syncthreads();
+      zero(acc);
+      blocks_mma<2, true>(acc, &Lk[0][0], PP, &Lo[0][0], PQ, ri, cj, NB);
+      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PQ + j] -= s; });
+      __syncthreads();
+      zero(acc);
+      blocks_mma<2, true>(acc, &XT1[0][0], PP, Cs, PQ, ri, cj, Kp1);
+      blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
+        if (i < g.kb1) g.R[int64_t(k1 + i) * d + c0 + j] = s;
+      });
+    }
   }
+  __syncthreads();  // the next tile overwrites Lo and Cs
 }
 
-// Grid: min(ntile, BLOCK_MAX_WG) workgroups (at least 1); workgroup b takes
-// tiles b, b + grid, ... The first tile's operands are loaded and its update
-// applied together with the diagonal block's, before the factorization.
-__global__ void __launch_bounds__(256)
-hinv_block(const BlockArgs g, int32_t* __restrict__ info) {
-  __shared__ double Lk[NB][PP];   // Lk[m][i] = L[k0 + i][s0 + m]
-  __shared__ double Xs[NB][PP];   // A_kk (lower part) during the factorization, then X_kk^T
-  __shared__ double Lo[NB][PQ];   // the tile's L_iS' or X_S'c; then the transposed row-tile output
-  __shared__ double Cs[NB * PQ];  // the tile's C
-  __shared__ __attribute__((aligned(16))) double bv[2][2][NB];
-  __shared__ int bad;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  const int bid = int(blockIdx.x);
-  const int d = g.d, k0 = g.k0, kb = g.kb, kl = g.kl;
-  // every load first: the diagonal block, the panel rows L_kS', and the
-  // first tile's operands
-  constexpr int PER = NB * NB / 256;
-  double av[PER], lk[PER], lo[8], cv[8];
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
-    const bool ok = i < kb && j <= i;
-    av[t] = g.A[ok ? int64_t(k0 + i) * d + k0 + j : int64_t(k0) * d + k0];
-    lk[t] = g.LT[i < kl ? int64_t(i) * d + k0 + (j < kb ? j : kb - 1) : 0];  // i = m, j = column in the block
-  }
-  const bool first = bid < g.ntile;
-  if (first) tile_load(g, bid, lo, cv);
-#pragma unroll
-  for (int t = 0; t < PER; ++t) {
-    const int e = tid + 256 * t, i = e >> 6, j = e & 63;
-    Xs[i][j] = (i < kb && j <= i) ? av[t] : 0.0;
-    Lk[i][j] = lk[t];
-  }
-  if (first) tile_stage(bid < g.nrow, lo, cv, Lo, Cs);
-  __syncthreads();
-  if (kl > 0) {
-    // the diagonal block: wave w, rows 16 w .. + 16, all four column blocks
-    doublex4 acc[4];
-    zero(acc);
-    const int ri[4] = {16 * wave, 16 * wave, 16 * wave, 16 * wave};
-    const int cj[4] = {0, 16, 32, 48};
-    blocks_mma<4, true>(acc, &Lk[0][0], PP, &Lk[0][0], PP, ri, cj, kl);
-    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Xs[i][j] -= s; });
-    if (first) tile_update(bid < g.nrow, kl, Lk, Lo, Cs);
-    __syncthreads();
-  }
-  double v[4][4], dr[4];
-  diag_factor(Xs, kb, v, dr, bv);  // reads Xs before its first barrier
+// X = D^-1/2 Y of one factorization (zero above the diagonal and past kb),
+// stored transposed in XT; workgroup 0 also writes it into R's diagonal
+// block at k and reports a pivot that is not positive (NaN included) as one
+// plus its index in H. Every thread has read the factorization's input from
+// XT before the factorization's first barrier.
+__device__ __forceinline__ void diag_finish(const StepArgs& g, int k, int kb, const double (&v)[4][4],
+                                            const double (&dr)[4], double (*XT)[PP], int* bad,
+                                            int32_t* __restrict__ info) {
+  const int tid = threadIdx.x;
   const int rb_ = 4 * (tid >> 4), cb_ = 4 * (tid & 15);
-  if (bid == 0) {
-    // The first pivot that is not positive (NaN included) sets `info` to one
-    // plus its index in H.
-    if (tid == 0) bad = NB;
+  if (blockIdx.x == 0) {
+    if (tid == 0) *bad = NB;
     __syncthreads();
     if (cb_ == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (rb_ + r < kb && !(dr[r] > 0.0)) atomicMin(&bad, rb_ + r);
+        if (rb_ + r < kb && !(dr[r] > 0.0)) atomicMin(bad, rb_ + r);
     }
     __syncthreads();
-    if (tid == 0 && bad < NB) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (d - 1 - (k0 + bad)));
+    if (tid == 0 && *bad < NB) atomicCAS(reinterpret_cast<int*>(info), 0, 1 + (g.d - 1 - (k + *bad)));
   }
-  // X_kk = D^-1/2 Y (zero above the diagonal and past kb), stored
-  // transposed in Xs; workgroup 0 also writes it into R's diagonal block.
-  // Every thread has read Xs in diag_factor before its first barrier.
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i = rb_ + r;
@@ -482,23 +477,74 @@ hinv_block(const BlockArgs g, int32_t* __restrict__ info) {
     for (int c = 0; c < 4; ++c) {
       const int j = cb_ + c;
       const double x = (i < kb && j <= i) ? v[r][c] * si : 0.0;
-      Xs[j][i] = x;
-      if (bid == 0 && i < kb && j < kb) g.R[int64_t(k0 + i) * d + k0 + j] = x;
+      XT[j][i] = x;
+      if (blockIdx.x == 0 && i < kb && j < kb) g.R[int64_t(k + i) * g.d + k + j] = x;
     }
   }
   __syncthreads();
-  for (int tb = bid; tb < g.ntile; tb += int(gridDim.x)) {
-    if (tb != bid) {
-      tile_load(g, tb, lo, cv);
-      __syncthreads();  // the previous tile is done with Lo and Cs
-      tile_stage(tb < g.nrow, lo, cv, Lo, Cs);
-      __syncthreads();
-      if (kl > 0) {
-        tile_update(tb < g.nrow, kl, Lk, Lo, Cs);
-        __syncthreads();
-      }
+}
+
+// Grid: min(ntile, STEP_MAX_WG) workgroups (at least 1); workgroup b takes
+// tiles b, b + grid, ...
+__global__ void __launch_bounds__(256)
+hinv_step(const StepArgs g, int32_t* __restrict__ info) {
+  __shared__ double XT0[NB][PP];  // A_k0k0 during its factorization, then X_k0^T
+  __shared__ double XT1[NB][PP];  // A_k1k1 during its factorization, then X_k1^T
+  __shared__ double Lk[NB][PP];   // A_k1k0 (row-major), then Lk[m][i] = L[k1 + i][k0 + m]
+  __shared__ double Lo[NB][PQ];   // the tile's L_ik0 (Lo[m][i]) or X_k0c (Lo[m][c])
+  __shared__ double Cs[NB * PQ];  // the tile's C: 32 x 64 at pitch PP (rows) or 64 x 32 at pitch PQ (columns)
+  __shared__ __attribute__((aligned(16))) double bv[2][2][NB];
+  __shared__ int bad;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int d = g.d, k0 = g.k0, k1 = k0 + NB, kb0 = g.kb0, kb1 = g.kb1;
+  constexpr int PER = NB * NB / 256;
+  {
+    double a00[PER], a10[PER], a11[PER];
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int e = tid + 256 * t, i = e >> 6, j = e & 63;
+      const bool ok00 = i < kb0 && j <= i;
+      const bool ok10 = i < kb1;
+      const bool ok11 = i < kb1 && j <= i;
+      a00[t] = g.A[ok00 ? int64_t(k0 + i) * d + k0 + j : int64_t(k0) * d + k0];
+      a10[t] = g.A[ok10 ? int64_t(k1 + i) * d + k0 + j : int64_t(k0) * d + k0];
+      a11[t] = g.A[ok11 ? int64_t(k1 + i) * d + k1 + j : int64_t(k0) * d + k0];
     }
-    tile_product(g, tb, Xs, Cs, Lo);
+#pragma unroll
+    for (int t = 0; t < PER; ++t) {
+      const int e = tid + 256 * t, i = e >> 6, j = e & 63;
+      XT0[i][j] = (i < kb0 && j <= i) ? a00[t] : 0.0;
+      Lk[i][j] = i < kb1 ? a10[t] : 0.0;
+      XT1[i][j] = (i < kb1 && j <= i) ? a11[t] : 0.0;
+    }
+  }
+  __syncthreads();
+  double v[4][4], dr[4];
+  diag_factor(XT0, kb0, v, dr, bv);
+  diag_finish(g, k0, kb0, v, dr, XT0, &bad, info);
+  if (kb1 > 0) {
+    // L_k1k0 = A_k1k0 X_k0^T: wave w, rows 16 w .. + 16, all four column
+    // blocks; Lk <- its transpose once every wave has read A_k1k0; then
+    // A_k1k1 -= L_k1k0 L_k1k0^T.
+    doublex4 acc[4];
+    zero(acc);
+    const int ri[4] = {16 * wave, 16 * wave, 16 * wave, 16 * wave};
+    const int cj[4] = {0, 16, 32, 48};
+    blocks_mma<4, false>(acc, &Lk[0][0], PP, &XT0[0][0], PP, ri, cj, NB);
+    __syncthreads();
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lk[j][i] = s; });
+    __syncthreads();
+    zero(acc);
+    blocks_mma<4, true>(acc, &Lk[0][0], PP, &Lk[0][0], PP, ri, cj, NB);
+    blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { XT1[i][j] -= s; });
+    __syncthreads();
+    diag_factor(XT1, kb1, v, dr, bv);
+    diag_finish(g, k1, kb1, v, dr, XT1, &bad, info);
+  }
+  for (int tb = int(blockIdx.x); tb < g.ntile; tb += int(gridDim.x)) {
+    double c0v[8], c1v[8];
+    step_load(g, tb, c0v, c1v);
+    step_tile(g, tb, c0v, c1v, XT0, XT1, Lk, Lo, Cs);
   }
 }
 
@@ -757,15 +803,14 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     const int s1 = di - s0 < KS ? di : s0 + KS;
     const double* LTp = w.LT + size_t(p % 2) * KS * di;
     double* LTw = w.LT + size_t(p % 2) * KS * di;
-    for (int k0 = s0; k0 < s1; k0 += NB) {
-      const int kb = s1 - k0 < NB ? s1 - k0 : NB;
-      const int kl = k0 - s0;
-      const int nrow = (di - k0 - kb + 31) / 32;
-      const int ntile = nrow + k0 / 32;
-      const int grid = ntile < 1 ? 1 : (ntile < BLOCK_MAX_WG ? ntile : BLOCK_MAX_WG);
-      const BlockArgs args{w.A, w.R, LTw, di, k0, kb, kl, nrow, ntile};
-      hipLaunchKernelGGL(hinv_block, dim3(unsigned(grid)), dim3(256), 0, s, args, info);
-    }
+    const int kb0 = s1 - s0 < NB ? s1 - s0 : NB;
+    const int kb1 = s1 - s0 - kb0;
+    const int nrow = (di - s1 + 31) / 32;
+    const int ncol = s0 / 32;
+    const int ntile = nrow + ncol + (kb1 > 0 ? 2 : 0);
+    const int grid = ntile < 1 ? 1 : (ntile < STEP_MAX_WG ? ntile : STEP_MAX_WG);
+    const StepArgs args{w.A, w.R, LTw, di, s0, kb0, kb1, nrow, ncol, ntile};
+    hipLaunchKernelGGL(hinv_step, dim3(unsigned(grid)), dim3(256), 0, s, args, info);
     if (s1 < di) {
       const int s2 = di - s1 < KS ? di : s1 + KS;
       if (ctx && p >= 1 && hipStreamWaitEvent(s, ctx->trail[(p - 1) % 2], 0) != hipSuccess) return GPTQ_E_HIP;
