@@ -470,15 +470,21 @@ syrk_f32_valu(const float* __restrict__ X, int64_t n_tokens, int d, int64_t ldx,
 }
 
 // H[i][j] = 2 * sum_s partial_s (min(i,j), max(i,j)) (+ H[i][j] if accumulate).
-// One 32x32 output block per workgroup; the source block (upper) is summed
-// into LDS in a fixed split order and written transposed where needed.
+// One 32x32 source block (SI <= SJ, upper) per workgroup: its partials are
+// read once and summed in a fixed split order in fp64, then the block is
+// written to (SI, SJ) and, transposed through LDS, to (SJ, SI). A block on
+// the diagonal mirrors its upper half.
 __global__ void __launch_bounds__(256)
 syrk_reduce(const float* __restrict__ partial, int T, int nb, int ntiles, int nsplit, int d,
             float* __restrict__ H, int accumulate) {
   __shared__ double blk[32][33];
   const int nob = (d + 31) / 32;
-  const int OI = blockIdx.x / nob, OJ = blockIdx.x % nob;
-  const int SI = OI < OJ ? OI : OJ, SJ = OI < OJ ? OJ : OI;  // source block, SI <= SJ
+  int b = int(blockIdx.x), SI = 0;
+  while (b >= nob - SI) {  // row SI of the upper triangle holds nob - SI blocks
+    b -= nob - SI;
+    ++SI;
+  }
+  const int SJ = SI + b;
   const int R0 = SI * 32, C0 = SJ * 32;
   const int bi = R0 / T, bj = C0 / T;
   const int tile = bi * nb - (bi * (bi - 1)) / 2 + (bj - bi);
@@ -506,19 +512,25 @@ syrk_reduce(const float* __restrict__ partial, int T, int nb, int ntiles, int ns
   __syncthreads();
   for (int e = tid; e < 32 * 32; e += 256) {
     const int r = e >> 5, c = e & 31;
-    const int gi = OI * 32 + r, gj = OJ * 32 + c;
-    if (gi >= d || gj >= d) continue;
-    double v;
-    if (OI < OJ)
-      v = blk[r][c];
-    else if (OI > OJ)
-      v = blk[c][r];
-    else
-      v = r <= c ? blk[r][c] : blk[c][r];
-    v *= 2.0;
-    const int64_t o = int64_t(gi) * d + gj;
-    if (accumulate) v += double(H[o]);
-    H[o] = float(v);
+    {
+      const int gi = R0 + r, gj = C0 + c;
+      if (gi < d && gj < d) {
+        double v = SI < SJ ? blk[r][c] : (r <= c ? blk[r][c] : blk[c][r]);
+        v *= 2.0;
+        const int64_t o = int64_t(gi) * d + gj;
+        if (accumulate) v += double(H[o]);
+        H[o] = float(v);
+      }
+    }
+    if (SI < SJ) {
+      const int gi = C0 + r, gj = R0 + c;
+      if (gi < d && gj < d) {
+        double v = blk[c][r] * 2.0;
+        const int64_t o = int64_t(gi) * d + gj;
+        if (accumulate) v += double(H[o]);
+        H[o] = float(v);
+      }
+    }
   }
 }
 
@@ -661,7 +673,7 @@ extern "C" int gptq_hessian_accumulate(const void* X, int xdtype, int64_t n_toke
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }
   const int nob = int((d + 31) / 32);
-  hipLaunchKernelGGL(syrk_reduce, dim3(unsigned(nob * nob)), dim3(256), 0, s, partial, p.T, p.nb, p.ntiles,
-                     p.nslot, int(d), H, accumulate);
+  hipLaunchKernelGGL(syrk_reduce, dim3(unsigned(nob * (nob + 1) / 2)), dim3(256), 0, s, partial, p.T, p.nb,
+                     p.ntiles, p.nslot, int(d), H, accumulate);
   return launch_status();
 }
