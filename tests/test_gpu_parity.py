@@ -166,6 +166,30 @@ def test_prepare_hinv_reports_indefinite(gpu, d):
     assert 1 <= int(hv.info.item()) <= d
 
 
+@pytest.mark.parametrize("bad", [[10], [70], [130], [200], [280], [70, 200], [200, 70]])
+def test_prepare_hinv_reports_the_first_breakdown(gpu, bad):
+    """info = 1 + the H column of the first pivot that is not positive, in
+    the factorization's order (H's columns from the last): a breakdown in
+    either block of a super-panel, in a later one, and in the last, single
+    block (d = 300 = 128 + 128 + 44 columns)."""
+    d = 300
+    h = np.ones(d, np.float32)
+    for a in bad:  # a: position in the factorization's order
+        h[d - 1 - a] = -1.0  # -1 + lambda < 0 with lambda = 0.01 * mean(diag H) < 0.01
+    hv = gpu.gptq_prepare_hinv(gpu_tensor(np.diag(h)), 0.01)
+    torch.cuda.synchronize()
+    assert int(hv.info.item()) == 1 + (d - 1 - min(bad))
+
+
+def test_prepare_hinv_nan_diagonal_fails_at_the_first_pivot(gpu):
+    d = 300
+    h = np.ones(d, np.float32)
+    h[100] = np.nan  # lambda is NaN, so every damped pivot is
+    hv = gpu.gptq_prepare_hinv(gpu_tensor(np.diag(h)), 0.01)
+    torch.cuda.synchronize()
+    assert int(hv.info.item()) == d
+
+
 # ------------------------------------------------------------------- sweep
 def oracle_u(d, seed, n=None):
     X = make_x(n or (4 * d + 64), d, np.float32, seed)
