@@ -13,20 +13,20 @@
 // J L^-1 J. The Cholesky factor with positive diagonal is unique, so this is
 // the factor of H_d^-1 itself.
 //
-// L and X = L^-1 are computed together in fp64, 64 columns at a time, with
-// the trailing update applied once per 128-column super-panel S = [s0, s1):
-//   block (one launch per 64 columns): every workgroup applies
-//         A_kk -= L_kS' L_kS'^T over the super-panel's earlier blocks S'
-//         (left-looking) and factors X_kk = chol(A_kk)^-1 itself (a pivot
-//         that is not positive sets `info`), then computes its tiles of
-//                  row blocks i > k:  L_ik = (A_ik - L_iS' L_kS'^T) X_kk^T,
-//                                     kept column-major in the panel buffer LT
-//                  col blocks c < k:  X_kc = X_kk (R_kc - L_kS' X_S'c)
+// L and X = L^-1 are computed together in fp64, one 128-column super-panel
+// S = [s0, s1) of two 64-column blocks k0, k1 at a time:
+//   step (one launch per super-panel): every workgroup factors both
+//         diagonal blocks itself, X_k0 = chol(A_k0k0)^-1 and, after
+//         A_k1k1 -= L_k1k0 L_k1k0^T with L_k1k0 = A_k1k0 X_k0^T,
+//         X_k1 = chol(A_k1k1)^-1 (a pivot that is not positive sets `info`),
+//         then computes its tiles of
+//                  rows i >= s1:  L_iS, kept column-major in the panel buffer LT
+//                  cols c < s1:   X_Sc = block row S of X
 //   trail (many, once per super-panel, K = 128):
 //                  A_ij -= L_iS L_jS^T   for i >= j >= s1 (lower tiles)
 //                  R_ic -= L_iS X_Sc     for i >= s1, c < s1
 // R starts as the identity; block row k of R becomes block row k of X once
-// its block step has run. All products use the fp64 MFMA
+// its super-panel step has run. All products use the fp64 MFMA
 // (v_mfma_f64_16x16x4f64). The trailing update, which holds almost all of
 // the flops, reads the trailing matrix once per 128 columns instead of once
 // per 64 and keeps 16 independent MFMA chains per wave.
@@ -770,11 +770,11 @@ extern "C" size_t gptq_prepare_hinv_workspace_size(int64_t d) {
 
 // Schedule (S = the caller's stream, X = the auxiliary stream). For each
 // super-panel p = [s0, s1), with s2 = s1 + KS:
-//   S: the block steps of p (writing the panel buffer LT[p % 2])
+//   S: the super-panel step of p (writing the panel buffer LT[p % 2])
 //   S: wait for X's trailing update of p - 1, then apply p to the next
 //      super-panel's columns [s1, s2) and R rows [s1, s2)   ("trail A")
 //   X: after trail A, apply p to everything at and beyond s2 ("trail B"),
-//      overlapping with the next super-panel's steps on S.
+//      overlapping with the next super-panel's step on S.
 // The two updates touch disjoint tiles; every pair that touches the same
 // tiles or panel buffer is ordered by an event.
 extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* lambda_out, int32_t* info,
