@@ -74,12 +74,27 @@ hinv_lambda(const float* __restrict__ H, int d, double damp, double* __restrict_
   }
 }
 
-// A[i][j] = H[d-1-j][d-1-i] + lambda [i == j] for j <= i (reads H's lower
-// triangle, which is the reversed matrix's lower triangle by symmetry).
-// One 32x32 lower block per workgroup.
+// A[i][j] = H[d-1-j][d-1-i] + lambda [i == j] and R[i][j] = [i == j] for
+// j <= i (reads H's lower triangle, which is the reversed matrix's lower
+// triangle by symmetry), one 32x32 lower block per workgroup. The
+// workgroups after the first nlow zero R on block rows [s0, s0 + 64) x
+// columns [s0 + 64, s0 + 128) of each super-panel with two blocks: the only
+// part of R above the diagonal that is read (by the trailing update, inside
+// block rows S of X) before a super-panel step writes it. Nothing reads the
+// rest of R above the diagonal.
 __global__ void __launch_bounds__(256)
-hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, double* __restrict__ A) {
+hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, double* __restrict__ A,
+           double* __restrict__ R, int nlow) {
   __shared__ float t[32][33];
+  if (int(blockIdx.x) >= nlow) {
+    const int u = int(blockIdx.x) - nlow;
+    const int i0 = (u >> 2) * KS + 32 * ((u >> 1) & 1), j0 = (u >> 2) * KS + NB + 32 * (u & 1);
+    for (int e = threadIdx.x; e < 1024; e += 256) {
+      const int i = i0 + (e >> 5), j = j0 + (e & 31);
+      if (i < d && j < d) R[int64_t(i) * d + j] = 0.0;
+    }
+    return;
+  }
   int b = blockIdx.x, bi = 0;
   while (b > bi) {
     b -= bi + 1;
@@ -99,20 +114,7 @@ hinv_setup(const float* __restrict__ H, int d, const double* __restrict__ lam, d
     const int i = i0 + ii, j = j0 + jj;
     if (i >= d || j >= d || j > i) continue;
     A[int64_t(i) * d + j] = double(t[jj][ii]) + (i == j ? l : 0.0);
-  }
-}
-
-// R = identity (both triangles: the panel and trailing products read R's
-// upper part inside finished block rows and rely on it being zero).
-__global__ void __launch_bounds__(256) hinv_eye(double* __restrict__ R, int d) {
-  const int64_t n = int64_t(d) * d;
-  for (int64_t e = (blockIdx.x * int64_t(256) + threadIdx.x) * 2; e < n; e += int64_t(gridDim.x) * 512) {
-    const int64_t i0 = e / d, j0 = e % d;
-    R[e] = (i0 == j0) ? 1.0 : 0.0;
-    if (e + 1 < n) {
-      const int64_t i1 = (e + 1) / d, j1 = (e + 1) % d;
-      R[e + 1] = (i1 == j1) ? 1.0 : 0.0;
-    }
+    R[int64_t(i) * d + j] = i == j ? 1.0 : 0.0;
   }
 }
 
@@ -791,9 +793,11 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
   hipStream_t x = ctx ? ctx->aux : s;
   hipLaunchKernelGGL(hinv_lambda, dim3(1), dim3(256), 0, s, H, di, damp, w.lam, lambda_out, info);
   const int nb32 = (di + 31) / 32;
-  hipLaunchKernelGGL(hinv_setup, dim3(unsigned(nb32 * (nb32 + 1) / 2)), dim3(256), 0, s, H, di, w.lam, w.A);
-  const int64_t eye_blocks = (int64_t(di) * di + 511) / 512;
-  hipLaunchKernelGGL(hinv_eye, dim3(unsigned(eye_blocks < 4096 ? eye_blocks : 4096)), dim3(256), 0, s, w.R, di);
+  const int nlow = nb32 * (nb32 + 1) / 2;
+  int nup = 0;  // 4 upper 32x32 blocks per super-panel with two blocks
+  for (int s0 = 0; s0 < di; s0 += KS)
+    if ((di - s0 < KS ? di - s0 : KS) > NB) nup += 4;
+  hipLaunchKernelGGL(hinv_setup, dim3(unsigned(nlow + nup)), dim3(256), 0, s, H, di, w.lam, w.A, w.R, nlow);
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   if (ctx) {
     if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(x, ctx->fork, 0) != hipSuccess)
