@@ -190,6 +190,33 @@ def test_prepare_hinv_nan_diagonal_fails_at_the_first_pivot(gpu):
     assert int(hv.info.item()) == d
 
 
+@pytest.mark.parametrize("d", [65, 300, 700])
+def test_stages_ignore_workspace_contents(gpu, d):
+    """Each stage gives the same result to the bit from a workspace of zero
+    bytes and from one of 0xff bytes (NaN in every float slot): no kernel
+    reads a workspace entry before a kernel of the same call wrote it."""
+    X = make_x(3 * d + 50, d, np.float16, d + 7)
+    Xg = gpu_tensor(X)
+    W = gpu_tensor((0.02 * np.random.default_rng(d).standard_normal((48, d))).astype(np.float16))
+    outs = []
+    for fill in (0, 255):
+        wsh = torch.full((gpu.gptq_hessian_workspace_size(Xg.shape[0], d, torch.float16),), fill, dtype=torch.uint8,
+                         device=DEV)
+        H = gpu.gptq_hessian_accumulate(Xg, ws=wsh)
+        wsu = torch.full((gpu.gptq_prepare_hinv_workspace_size(d),), fill, dtype=torch.uint8, device=DEV)
+        hv = gpu.gptq_prepare_hinv(H, 0.01, ws=wsu)
+        wsq = torch.full((gpu.gptq_quantize_layer_workspace_size(48, d, 4, 32, 128),), fill, dtype=torch.uint8,
+                         device=DEV)
+        q = gpu.gptq_quantize_layer(W, hv.U, 4, 32, 128, ws=wsq)
+        torch.cuda.synchronize()
+        assert int(hv.info.item()) == 0
+        outs.append([H.cpu(), hv.U.cpu(), q.codes.cpu(), q.scales.cpu(), q.row_loss.cpu()])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    U_ref, _ = O.prepare_hinv(O.hessian(X), 0.01)
+    assert rel_fro(outs[1][1].numpy(), U_ref) < 1e-5
+
+
 # ------------------------------------------------------------------- sweep
 def oracle_u(d, seed, n=None):
     X = make_x(n or (4 * d + 64), d, np.float32, seed)
