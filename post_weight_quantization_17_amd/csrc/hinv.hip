@@ -22,7 +22,8 @@
 //         then computes its tiles of
 //                  rows i >= s1:  L_iS, kept column-major in the panel buffer LT
 //                  cols c < s1:   X_Sc = block row S of X
-//   trail (many, once per super-panel, K = 128):
+//   trail (once per super-panel, K = 128; the next super-panel's columns
+//         take the previous super-panel too, K = 256):
 //                  A_ij -= L_iS L_jS^T   for i >= j >= s1 (lower tiles)
 //                  R_ic -= L_iS X_Sc     for i >= s1, c < s1
 // R starts as the identity; block row k of R becomes block row k of X once
@@ -30,6 +31,8 @@
 // (v_mfma_f64_16x16x4f64). The trailing update, which holds almost all of
 // the flops, reads the trailing matrix once per 128 columns instead of once
 // per 64 and keeps 16 independent MFMA chains per wave.
+#include <hip/hip_ext.h>
+
 #include <mutex>
 #include <utility>
 
@@ -557,22 +560,27 @@ hinv_step(const StepArgs g, int32_t* __restrict__ info) {
 //                     a rectangle from (ra0, ca0)
 //   blocks [nA, ..):  R tiles, rows from rr0, columns T tc < s1:
 //                     R_ic -= L_iS X_Sc
+// With p0 < s0 the tile first applies the earlier super-panel P = [p0, s0)
+// from its own panel buffer LT0 (A_ij -= L_iP L_jP^T; R_ic -= L_iP X_Pc for
+// tiles left of s0, since X_Pc is zero for c >= s0), accumulating both in the
+// same registers: K = (s0 - p0) + (s1 - s0), in the order P then S.
 // Each wave owns a (T/2) x (T/2) quarter (T = 128: 16 independent MFMA
 // chains; T = 64, used when big tiles would leave CUs idle: 4 chains). The
 // operands (L_S column-major in LT; X_S as rows s0.. of R) pass through LDS
 // in chunks of 16 k; the next chunk's loads are in flight while the current
 // one is multiplied. The accumulators start from the old tile, so it is read
 // once and written once.
-constexpr int TK = 16;  // k per LDS chunk
 struct TrailSpec {
   int s0, s1;     // the super-panel whose columns are applied (K = s1 - s0)
   int ra0, naR;   // A part: first row (and, if tri, first column), tile rows
   int ca0, naC;   // A part: first column and tile columns of a rectangle; naC = 0: lower triangle
   int rr0, nrR;   // R part: first row, tile rows (columns: tiles 0 .. s1 / T)
+  int p0;         // earlier super-panel [p0, s0) applied first; p0 = s0: none
 };
-template <int T>
-__device__ __forceinline__ void trail_tile(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT,
-                                           int d, const TrailSpec& sp, int tile, double (*As)[T + 4],
+template <int T, int TK>
+__device__ __forceinline__ void trail_tile(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT0,
+                                           const double* __restrict__ LT, int d, const TrailSpec& sp, int tile,
+                                           double (*As)[T + 4],
                                            double (*Bs)[T + 4]) {
   constexpr int BL = T / 32;           // 16x16 blocks per wave dimension
   constexpr int STEP = 256 / T;        // k rows loaded per pass
@@ -582,7 +590,6 @@ __device__ __forceinline__ void trail_tile(double* __restrict__ A, double* __res
   const int wr = wave >> 1, wc = wave & 1;
   const int lr = lane & 15, lk = lane >> 4;
   const int s0 = sp.s0, s1 = sp.s1;
-  const int K = s1 - s0;
   const bool tri = sp.naC == 0;
   const int nA = tri ? sp.naR * (sp.naR + 1) / 2 : sp.naR * sp.naC;
   int b = tile;
@@ -608,18 +615,37 @@ __device__ __forceinline__ void trail_tile(double* __restrict__ A, double* __res
     c0 = T * (b / sp.nrR);
   }
   double* __restrict__ M = apart ? A : R;
-  // chunk loads: thread t covers column t % T of k rows t / T + STEP u
+  // k runs over [0, K0) for the earlier super-panel (R tiles at or right of
+  // s0 take none of it), then over [K0, K) for S
+  const int K0 = (apart || c0 < s0) ? s0 - sp.p0 : 0;
+  const int K = K0 + (s1 - s0);
+  // chunk loads: thread t covers column t % T of k rows t / T + STEP u,
+  // at per-thread bases plus a chunk offset that is the same for all threads
   const int li = tid % T, lk0 = tid / T;
   const int ga = r0 + li < d ? r0 + li : d - 1;
   const int gb = c0 + li < d ? c0 + li : d - 1;
-  const double* __restrict__ srcA = LT + ga;
-  const double* __restrict__ srcB = apart ? LT + gb : R + int64_t(s0) * d + gb;
+  const double* __restrict__ srcA = LT0 + ga;
+  const double* __restrict__ srcB = apart ? LT0 + gb : R + gb;
+  const int64_t dLT = LT - LT0;
+  auto chunk = [&](int kc, int64_t& oa, int64_t& ob) {
+    if (kc < K0) {
+      oa = int64_t(kc) * d;
+      ob = apart ? oa : int64_t(sp.p0 + kc) * d;
+    } else {
+      oa = dLT + int64_t(kc - K0) * d;
+      ob = apart ? oa : int64_t(s0 + kc - K0) * d;
+    }
+  };
   double la[U], lb[U];
+  {
+    int64_t oa, ob;
+    chunk(0, oa, ob);
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t o = int64_t(lk0 + STEP * u) * d;
-    la[u] = srcA[o];
-    lb[u] = srcB[o];
+    for (int u = 0; u < U; ++u) {
+      const int64_t o = int64_t(lk0 + STEP * u) * d;
+      la[u] = srcA[oa + o];
+      lb[u] = srcB[ob + o];
+    }
   }
   // old tile into the accumulators (clamped addresses; rows past d and the
   // upper half of diagonal A tiles are computed but never stored)
@@ -645,11 +671,13 @@ __device__ __forceinline__ void trail_tile(double* __restrict__ A, double* __res
     }
     __syncthreads();
     if (kc + TK < K) {
+      int64_t oa, ob;
+      chunk(kc + TK, oa, ob);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t o = int64_t(kc + TK + lk0 + STEP * u) * d;
-        la[u] = srcA[o];
-        lb[u] = srcB[o];
+        const int64_t o = int64_t(lk0 + STEP * u) * d;
+        la[u] = srcA[oa + o];
+        lb[u] = srcB[ob + o];
       }
     }
 #pragma unroll
@@ -678,13 +706,14 @@ __device__ __forceinline__ void trail_tile(double* __restrict__ A, double* __res
       }
 }
 
-// One tile per workgroup.
-template <int T>
+// One tile per workgroup; TK = k per LDS chunk.
+template <int T, int TK>
 __global__ void __launch_bounds__(256, 2)
-hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT, int d, TrailSpec sp) {
+hinv_trail(double* __restrict__ A, double* __restrict__ R, const double* __restrict__ LT0,
+           const double* __restrict__ LT, int d, TrailSpec sp) {
   __shared__ double As[TK][T + 4];  // As[k][i] = -L[r0 + i][s0 + k]
   __shared__ double Bs[TK][T + 4];  // Bs[k][j] = L[c0 + j][s0 + k] or X[s0 + k][c0 + j]
-  trail_tile<T>(A, R, LT, d, sp, blockIdx.x, As, Bs);
+  trail_tile<T, TK>(A, R, LT0, LT, d, sp, blockIdx.x, As, Bs);
 }
 
 // U[i][j] = X[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -697,6 +726,10 @@ hinv_write_u(const double* __restrict__ R, int d, float* __restrict__ U) {
   }
 }
 
+// Panel buffers: super-panel p writes buffer p % NPANEL, which the trailing
+// updates of p and p + 1 read.
+constexpr int NPANEL = 3;
+
 struct HinvWs {
   double *A, *R, *LT, *lam;
   size_t bytes;
@@ -705,7 +738,7 @@ struct HinvWs {
 HinvWs carve(void* ws, int64_t d) {
   HinvWs w{};
   const size_t mat = align_up(size_t(d) * d * sizeof(double), 256);
-  const size_t panel = align_up(size_t(2) * KS * d * sizeof(double), 256);  // double buffered
+  const size_t panel = align_up(size_t(NPANEL) * KS * d * sizeof(double), 256);
   char* p = static_cast<char*>(ws);
   w.A = reinterpret_cast<double*>(p);
   w.R = reinterpret_cast<double*>(p + mat);
@@ -720,7 +753,7 @@ HinvWs carve(void* ws, int64_t d) {
 // concurrent callers cannot interleave their event records.
 struct AuxCtx {
   hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, chain[2] = {}, trail[2] = {};
+  hipEvent_t fork = nullptr, join = nullptr, chain[NPANEL] = {}, trail[NPANEL] = {};
   bool ready = false;
 };
 std::mutex g_aux_mu;
@@ -732,7 +765,11 @@ AuxCtx* aux_context() {
   AuxCtx& c = g_aux[dev];
   if (!c.ready) {
     if (hipStreamCreateWithFlags(&c.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    hipEvent_t* evs[6] = {&c.fork, &c.join, &c.chain[0], &c.chain[1], &c.trail[0], &c.trail[1]};
+    hipEvent_t* evs[2 + 2 * NPANEL] = {&c.fork, &c.join};
+    for (int i = 0; i < NPANEL; ++i) {
+      evs[2 + i] = &c.chain[i];
+      evs[2 + NPANEL + i] = &c.trail[i];
+    }
     for (hipEvent_t* e : evs)
       if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return nullptr;
     c.ready = true;
@@ -740,7 +777,16 @@ AuxCtx* aux_context() {
   return &c;
 }
 
-void launch_trail(hipStream_t st, const HinvWs& w, const double* LT, int d, TrailSpec sp, bool allow128) {
+// bulk: the update beyond the next super-panel (throughput-bound: 128x128
+// tiles while there are at least 4 per CU, 64x64 below that; 16 k per chunk).
+// look-ahead: the next super-panel's strip (K = 256), on the critical path
+// and bound by the latency of its dependent chunk loads: 32 k per chunk, and
+// 32x32 tiles while 64x64 ones would not give every CU one. A non-null
+// `done` is recorded by the launch itself, at the kernel's completion, which
+// leaves no gap on the stream as a separate record does (if nothing is
+// launched, it is recorded separately).
+void launch_trail(hipStream_t st, const HinvWs& w, const double* LT0, const double* LT, int d, TrailSpec sp,
+                  bool bulk, hipEvent_t done = nullptr) {
   auto tiles = [&](int T, TrailSpec& q) -> int64_t {
     q = sp;
     const int rows = d - sp.ra0;
@@ -751,12 +797,29 @@ void launch_trail(hipStream_t st, const HinvWs& w, const double* LT, int d, Trai
     return nA + int64_t(q.nrR) * (sp.s1 / T);
   };
   TrailSpec q;
-  const int64_t n128 = allow128 ? tiles(128, q) : 0;
-  if (allow128 && n128 >= 4 * 256) {
-    hipLaunchKernelGGL(hinv_trail<128>, dim3(unsigned(n128)), dim3(256), 0, st, w.A, w.R, LT, d, q);
+  if (!bulk) {
+    const int64_t n64 = tiles(64, q);
+    if (n64 >= 256) {
+      hipExtLaunchKernelGGL((hinv_trail<64, 32>), dim3(unsigned(n64)), dim3(256), 0, st, nullptr, done, 0, w.A, w.R,
+                            static_cast<const double*>(LT0), static_cast<const double*>(LT), d, q);
+      return;
+    }
+    const int64_t n32 = tiles(32, q);
+    if (n32 > 0) {
+      hipExtLaunchKernelGGL((hinv_trail<32, 32>), dim3(unsigned(n32)), dim3(256), 0, st, nullptr, done, 0, w.A, w.R,
+                            static_cast<const double*>(LT0), static_cast<const double*>(LT), d, q);
+      return;
+    }
+    if (done != nullptr) hipEventRecord(done, st);
+    return;
+  }
+  const int64_t n128 = tiles(128, q);
+  if (n128 >= 4 * 256) {
+    hipLaunchKernelGGL((hinv_trail<128, 16>), dim3(unsigned(n128)), dim3(256), 0, st, w.A, w.R, LT0, LT, d, q);
   } else {
     const int64_t n64 = tiles(64, q);
-    if (n64 > 0) hipLaunchKernelGGL(hinv_trail<64>, dim3(unsigned(n64)), dim3(256), 0, st, w.A, w.R, LT, d, q);
+    if (n64 > 0)
+      hipLaunchKernelGGL((hinv_trail<64, 16>), dim3(unsigned(n64)), dim3(256), 0, st, w.A, w.R, LT0, LT, d, q);
   }
 }
 
@@ -770,15 +833,20 @@ extern "C" size_t gptq_prepare_hinv_workspace_size(int64_t d) {
   return carve(nullptr, d).bytes;
 }
 
-// Schedule (S = the caller's stream, X = the auxiliary stream). For each
-// super-panel p = [s0, s1), with s2 = s1 + KS:
-//   S: the super-panel step of p (writing the panel buffer LT[p % 2])
-//   S: wait for X's trailing update of p - 1, then apply p to the next
-//      super-panel's columns [s1, s2) and R rows [s1, s2)   ("trail A")
-//   X: after trail A, apply p to everything at and beyond s2 ("trail B"),
-//      overlapping with the next super-panel's step on S.
-// The two updates touch disjoint tiles; every pair that touches the same
-// tiles or panel buffer is ordered by an event.
+// Schedule (S = the caller's stream, X = the auxiliary stream). Strip q is
+// super-panel q's columns of A and its rows of R. For each super-panel
+// p = [s0, s1):
+//   S: the super-panel step of p (writing the panel buffer LT[p % 3])
+//   S: "trail A": apply p - 1 and p (K = 256; p alone for p = 0) to strip
+//      p + 1, after waiting for trail B of p - 2, the last other writer of
+//      that strip
+//   X: after trail A, "trail B": apply p to strips p + 3 and beyond,
+//      overlapping the next super-panel steps on S
+// Trail B of p - 1 stops short of strip p + 1, so trail A never waits for the
+// trail B just launched beside it: the one it waits for had two super-panel
+// steps to finish. The writers of each tile and panel buffer are ordered by
+// stream order or an event: trail A of p waits for trail B of p - 2, which is
+// also the last reader of the buffer that step p + 1 overwrites.
 extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* lambda_out, int32_t* info,
                                  void* ws, size_t ws_bytes, void* stream) {
   if (d < 1 || d > 65536 || H == nullptr || U == nullptr || info == nullptr) return GPTQ_E_INVALID_ARG;
@@ -805,8 +873,7 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
   }
   for (int p = 0, s0 = 0; s0 < di; ++p, s0 += KS) {
     const int s1 = di - s0 < KS ? di : s0 + KS;
-    const double* LTp = w.LT + size_t(p % 2) * KS * di;
-    double* LTw = w.LT + size_t(p % 2) * KS * di;
+    double* LTw = w.LT + size_t(p % NPANEL) * KS * di;
     const int kb0 = s1 - s0 < NB ? s1 - s0 : NB;
     const int kb1 = s1 - s0 - kb0;
     const int nrow = (di - s1 + 31) / 32;
@@ -817,18 +884,21 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     hipLaunchKernelGGL(hinv_step, dim3(unsigned(grid)), dim3(256), 0, s, args, info);
     if (s1 < di) {
       const int s2 = di - s1 < KS ? di : s1 + KS;
-      if (ctx && p >= 1 && hipStreamWaitEvent(s, ctx->trail[(p - 1) % 2], 0) != hipSuccess) return GPTQ_E_HIP;
-      // trail A: columns [s1, s2) of A (all rows below), rows [s1, s2) of R
-      launch_trail(s, w, LTp, di, TrailSpec{s0, s1, s1, 0, s1, s2 - s1, s1, s2 - s1}, false);
-      // trail B: A at and beyond s2 (lower triangle), R rows from s2. It
+      const int s3 = di - s2 < KS ? di : s2 + KS;
+      if (ctx && p >= 2 && hipStreamWaitEvent(s, ctx->trail[(p - 2) % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
+      // trail A: columns [s1, s2) of A (all rows below), rows [s1, s2) of R,
+      // from super-panels p - 1 (whose trail B left them out) and p
+      const int p0 = p >= 1 ? s0 - KS : s0;
+      const double* LT0 = p >= 1 ? w.LT + size_t((p - 1) % NPANEL) * KS * di : LTw;
+      launch_trail(s, w, LT0, LTw, di, TrailSpec{s0, s1, s1, 0, s1, s2 - s1, s1, s2 - s1, p0}, false,
+                   ctx ? ctx->chain[p % NPANEL] : nullptr);
+      if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+      // trail B: A at and beyond s3 (lower triangle), R rows from s3. It
       // starts once trail A is done, so that trail A (on the critical path)
       // has the GPU to itself and trail B overlaps the next panel steps.
-      if (ctx) {
-        if (hipEventRecord(ctx->chain[p % 2], s) != hipSuccess) return GPTQ_E_HIP;
-        if (hipStreamWaitEvent(x, ctx->chain[p % 2], 0) != hipSuccess) return GPTQ_E_HIP;
-      }
-      if (s2 < di) launch_trail(x, w, LTp, di, TrailSpec{s0, s1, s2, 0, 0, 0, s2, di - s2}, true);
-      if (ctx && hipEventRecord(ctx->trail[p % 2], x) != hipSuccess) return GPTQ_E_HIP;
+      if (ctx && hipStreamWaitEvent(x, ctx->chain[p % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
+      if (s3 < di) launch_trail(x, w, LTw, LTw, di, TrailSpec{s0, s1, s3, 0, 0, 0, s3, di - s3, s0}, true);
+      if (ctx && hipEventRecord(ctx->trail[p % NPANEL], x) != hipSuccess) return GPTQ_E_HIP;
     }
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }

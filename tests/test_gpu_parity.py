@@ -129,7 +129,7 @@ def test_hessian_accumulate_strided_and_empty(gpu):
 
 
 # ---------------------------------------------------- inverse-Hessian factor
-@pytest.mark.parametrize("d", [1, 2, 63, 64, 65, 130, 256, 700])
+@pytest.mark.parametrize("d", [1, 2, 63, 64, 65, 130, 256, 700, 1500])
 def test_prepare_hinv_parity(gpu, d):
     say("hinv", d)
     X = make_x(3 * d + 50, d, np.float32, d)
