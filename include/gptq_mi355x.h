@@ -95,7 +95,10 @@ int gptq_hessian_accumulate(const void* X, int xdtype, int64_t n_tokens, int64_t
  *              numerically positive definite, k - 1 being the column (in H's
  *              indexing) where the factorization broke down. U is then
  *              unspecified.
- * The factorization runs in fp64 on the device. Errors: d < 1, NULL H, U
+ * The factorization runs in fp64 on the device. Part of its work runs on a
+ * per-device auxiliary stream that is forked from and joined back to
+ * `stream` by events within the call, so the call keeps the usual stream
+ * semantics and can be captured into a HIP graph. Errors: d < 1, NULL H, U
  * or info, damp < 0 or not finite -> GPTQ_E_INVALID_ARG.
  * ---------------------------------------------------------------------- */
 size_t gptq_prepare_hinv_workspace_size(int64_t d);

@@ -859,6 +859,12 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
   AuxCtx* ctx = aux_context();
 
   hipStream_t x = ctx ? ctx->aux : s;
+  // Under stream capture the events are recorded by hipEventRecord, whose
+  // capture semantics are the documented ones; otherwise trail A's launch
+  // records its event itself.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess) return GPTQ_E_HIP;
+  const bool by_launch = ctx && cap == hipStreamCaptureStatusNone;
   hipLaunchKernelGGL(hinv_lambda, dim3(1), dim3(256), 0, s, H, di, damp, w.lam, lambda_out, info);
   const int nb32 = (di + 31) / 32;
   const int nlow = nb32 * (nb32 + 1) / 2;
@@ -891,8 +897,9 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
       const int p0 = p >= 1 ? s0 - KS : s0;
       const double* LT0 = p >= 1 ? w.LT + size_t((p - 1) % NPANEL) * KS * di : LTw;
       launch_trail(s, w, LT0, LTw, di, TrailSpec{s0, s1, s1, 0, s1, s2 - s1, s1, s2 - s1, p0}, false,
-                   ctx ? ctx->chain[p % NPANEL] : nullptr);
+                   by_launch ? ctx->chain[p % NPANEL] : nullptr);
       if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+      if (ctx && !by_launch && hipEventRecord(ctx->chain[p % NPANEL], s) != hipSuccess) return GPTQ_E_HIP;
       // trail B: A at and beyond s3 (lower triangle), R rows from s3. It
       // starts once trail A is done, so that trail A (on the critical path)
       // has the GPU to itself and trail B overlaps the next panel steps.

@@ -190,6 +190,39 @@ def test_prepare_hinv_nan_diagonal_fails_at_the_first_pivot(gpu):
     assert int(hv.info.item()) == d
 
 
+@pytest.mark.parametrize("d", [300, 700])
+def test_prepare_hinv_under_graph_capture(gpu, d):
+    """The factor's two streams captured into one HIP graph: every replay, with
+    eager work and eager factor calls between replays, gives the eager U, lambda
+    and info to the bit."""
+    say("hinv graph", d)
+    X = make_x(3 * d + 50, d, np.float32, d + 7)
+    H = gpu_tensor(O.hessian(X).astype(np.float32))
+    ws = torch.empty(gpu.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=DEV)
+    ref = gpu.gptq_prepare_hinv(H, 0.01, ws=ws)  # also creates the auxiliary stream before capture
+    torch.cuda.synchronize()
+    assert int(ref.info.item()) == 0
+    out = gpu.Hinv(torch.empty_like(ref.U), torch.empty_like(ref.lam), torch.empty_like(ref.info))
+    wsg = torch.empty_like(ws)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu.gptq_prepare_hinv(H, 0.01, ws=wsg, out=out)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out.U.fill_(float("nan"))
+        out.info.fill_(-1)
+        wsg.fill_(255)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.U.view(torch.int32), ref.U.view(torch.int32))
+        assert torch.equal(out.lam, ref.lam) and int(out.info.item()) == 0
+        again = gpu.gptq_prepare_hinv(H, 0.01, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(again.U.view(torch.int32), ref.U.view(torch.int32))
+    U, _ = O.prepare_hinv(O.hessian(X).astype(np.float32).astype(np.float64), 0.01)
+    assert rel_fro(out.U.cpu().numpy(), U) < 1e-6
+
+
 @pytest.mark.parametrize("d", [65, 300, 700])
 def test_stages_ignore_workspace_contents(gpu, d):
     """Each stage gives the same result to the bit from a workspace of zero
