@@ -8,6 +8,8 @@ each row's first mismatch one step away at a decision the oracle took within
 first mismatch; loss within 1%; packed words bit-exact for the same codes.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -221,6 +223,52 @@ def test_prepare_hinv_under_graph_capture(gpu, d):
         assert torch.equal(again.U.view(torch.int32), ref.U.view(torch.int32))
     U, _ = O.prepare_hinv(O.hessian(X).astype(np.float32).astype(np.float64), 0.01)
     assert rel_fro(out.U.cpu().numpy(), U) < 1e-6
+
+
+def test_layer_path_under_graph_capture(gpu):
+    """Hessian, factor and sweep (with packing and loss) captured into one HIP
+    graph: three replays, with eager layer calls between them, give the eager
+    outputs to the bit."""
+    cfg = small(CONFIGS["attn_proj_4096x4096_4bit_g128"], d_row=96, d_col=640, n_tokens=9000)
+    say("layer graph", cfg.name, cfg.d_row, cfg.d_col, cfg.n_tokens)
+    Xd = torch.from_numpy(activations(cfg, threads=1)).to(DEV)
+    Wd = torch.from_numpy(weights(cfg)).to(DEV)
+
+    def layer(H=None, hws=None, fws=None, hv=None, qws=None, q=None):
+        H = gpu.gptq_hessian_accumulate(Xd, H=H, ws=hws)
+        hv = gpu.gptq_prepare_hinv(H, cfg.damp, ws=fws, out=hv)
+        return H, hv, gpu.gptq_quantize_layer(Wd, hv.U, cfg.bits, cfg.group_size, cfg.block, ws=qws, out=q)
+
+    He, hve, qe = layer()
+    torch.cuda.synchronize()
+    like = lambda t: None if t is None else torch.empty_like(t)
+    H = torch.empty_like(He)
+    hws = torch.empty(gpu.gptq_hessian_workspace_size(cfg.n_tokens, cfg.d_col, Xd.dtype), dtype=torch.uint8, device=DEV)
+    fws = torch.empty(gpu.gptq_prepare_hinv_workspace_size(cfg.d_col), dtype=torch.uint8, device=DEV)
+    qws = torch.empty(
+        gpu.gptq_quantize_layer_workspace_size(cfg.d_row, cfg.d_col, cfg.bits, cfg.group_size, cfg.block),
+        dtype=torch.uint8, device=DEV)
+    hv = gpu.Hinv(like(hve.U), like(hve.lam), like(hve.info))
+    q = gpu.Quantized(*(like(getattr(qe, f.name)) for f in dataclasses.fields(gpu.Quantized)))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(H, hws, fws, hv, qws, q)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for t in (H, hv.U, q.scales, q.loss):
+            t.fill_(float("nan"))
+        for t in (hws, fws, qws, q.codes, q.packed, q.zeros):
+            t.fill_(255 if t.dtype == torch.uint8 else -1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(H.view(torch.int32), He.view(torch.int32))
+        assert torch.equal(hv.U.view(torch.int32), hve.U.view(torch.int32)) and int(hv.info.item()) == 0
+        for f in dataclasses.fields(gpu.Quantized):
+            a, b = getattr(q, f.name), getattr(qe, f.name)
+            if b is not None:
+                assert torch.equal(a.reshape(-1).view(torch.uint8), b.reshape(-1).view(torch.uint8)), f.name
+        layer()
+        torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("d", [65, 300, 700])
