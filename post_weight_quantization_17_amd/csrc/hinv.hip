@@ -207,8 +207,13 @@ __device__ __forceinline__ double recip(double x) {
 // registers for all 64 steps; the 16 threads that hold rows j and j+1 (one
 // quarter of one wave) write them to LDS, double buffered, one barrier per
 // two steps.
-constexpr int PP = NB + 4;  // LDS pitch (doubles) of 64-wide tiles
-constexpr int PQ = 32 + 4;  // LDS pitch of 32-wide tiles
+// LDS pitches (doubles) of 64-wide and 32-wide tiles. They are odd so that
+// the 16 rows one quarter-wave reads in a row-major MFMA operand read (and
+// the 16 columns a transposing store writes) fall in distinct banks: with a
+// pitch of 68 those reads met 4 ways in a bank.
+constexpr int PP = NB + 1;
+constexpr int PQ = 32 + 1;
+static_assert(NB * PQ >= 32 * PP, "the tile buffer holds 32 x 64 at pitch PP");
 // Workgroups of one super-panel step. Each factors the diagonal blocks
 // itself, so more workgroups take CU time from the trailing update running
 // beside them; beyond this count a workgroup takes several tiles.
@@ -359,7 +364,9 @@ __device__ __forceinline__ void step_tile(const StepArgs& g, int tb, const doubl
                                           const double (*XT0)[PP], const double (*XT1)[PP], const double (*Lk)[PP],
                                           double (*Lo)[PQ], double* Cs) {
   const int tid = threadIdx.x, wave = tid >> 6, d = g.d, k1 = g.k0 + NB;
-  const int Kp0 = (g.kb0 + 3) & ~3, Kp1 = (g.kb1 + 3) & ~3;
+  // Every product runs over all 64 k, a compile-time count the compiler
+  // unrolls and pipelines: the operands are zero past kb0 / kb1 (the tile
+  // loads zero-fill, X^T and L_k1k0 are zero outside the block).
   const bool two = g.kb1 > 0;
   doublex4 acc[2];
   if (tb < g.nrow) {
@@ -374,7 +381,7 @@ __device__ __forceinline__ void step_tile(const StepArgs& g, int tb, const doubl
     }
     __syncthreads();
     zero(acc);
-    blocks_mma<2, false>(acc, Cs, PP, &XT0[0][0], PP, ri, cj, Kp0);
+    blocks_mma<2, false>(acc, Cs, PP, &XT0[0][0], PP, ri, cj, NB);
     // transpose through LDS, then coalesced stores: Lo[m][i] = L_ik0
     blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lo[j][i] = s; });
     __syncthreads();
@@ -395,7 +402,7 @@ __device__ __forceinline__ void step_tile(const StepArgs& g, int tb, const doubl
       blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PP + j] -= s; });
       __syncthreads();
       zero(acc);
-      blocks_mma<2, false>(acc, Cs, PP, &XT1[0][0], PP, ri, cj, Kp1);
+      blocks_mma<2, false>(acc, Cs, PP, &XT1[0][0], PP, ri, cj, NB);
       blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Lo[j][i] = s; });  // L_ik1
       __syncthreads();
 #pragma unroll
@@ -418,7 +425,7 @@ __device__ __forceinline__ void step_tile(const StepArgs& g, int tb, const doubl
       __syncthreads();
       // X_k0c = X_k0 C, the A operand X_k0[i][m] read k-major from X_k0^T
       zero(acc);
-      blocks_mma<2, true>(acc, &XT0[0][0], PP, Cs, PQ, ri, cj, Kp0);
+      blocks_mma<2, true>(acc, &XT0[0][0], PP, Cs, PQ, ri, cj, NB);
       blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
         Lo[i][j] = s;
         if (i < g.kb0) g.R[int64_t(g.k0 + i) * d + c0 + j] = s;
@@ -444,7 +451,7 @@ __device__ __forceinline__ void step_tile(const StepArgs& g, int tb, const doubl
       blocks_for_each(acc, ri, cj, [&](int i, int j, double s) { Cs[i * PQ + j] -= s; });
       __syncthreads();
       zero(acc);
-      blocks_mma<2, true>(acc, &XT1[0][0], PP, Cs, PQ, ri, cj, Kp1);
+      blocks_mma<2, true>(acc, &XT1[0][0], PP, Cs, PQ, ri, cj, NB);
       blocks_for_each(acc, ri, cj, [&](int i, int j, double s) {
         if (i < g.kb1) g.R[int64_t(k1 + i) * d + c0 + j] = s;
       });
@@ -784,8 +791,9 @@ AuxCtx* aux_context() {
 // 32x32 tiles while 64x64 ones would not give every CU one. A non-null
 // `done` is recorded by the launch itself, at the kernel's completion, which
 // leaves no gap on the stream as a separate record does (if nothing is
-// launched, it is recorded separately).
-void launch_trail(hipStream_t st, const HinvWs& w, const double* LT0, const double* LT, int d, TrailSpec sp,
+// launched, it is recorded separately). Launch errors are left for
+// hipGetLastError; the return value reports a failed separate record.
+bool launch_trail(hipStream_t st, const HinvWs& w, const double* LT0, const double* LT, int d, TrailSpec sp,
                   bool bulk, hipEvent_t done = nullptr) {
   auto tiles = [&](int T, TrailSpec& q) -> int64_t {
     q = sp;
@@ -802,16 +810,15 @@ void launch_trail(hipStream_t st, const HinvWs& w, const double* LT0, const doub
     if (n64 >= 256) {
       hipExtLaunchKernelGGL((hinv_trail<64, 32>), dim3(unsigned(n64)), dim3(256), 0, st, nullptr, done, 0, w.A, w.R,
                             static_cast<const double*>(LT0), static_cast<const double*>(LT), d, q);
-      return;
+      return true;
     }
     const int64_t n32 = tiles(32, q);
     if (n32 > 0) {
       hipExtLaunchKernelGGL((hinv_trail<32, 32>), dim3(unsigned(n32)), dim3(256), 0, st, nullptr, done, 0, w.A, w.R,
                             static_cast<const double*>(LT0), static_cast<const double*>(LT), d, q);
-      return;
+      return true;
     }
-    if (done != nullptr) hipEventRecord(done, st);
-    return;
+    return done == nullptr || hipEventRecord(done, st) == hipSuccess;
   }
   const int64_t n128 = tiles(128, q);
   if (n128 >= 4 * 256) {
@@ -821,6 +828,7 @@ void launch_trail(hipStream_t st, const HinvWs& w, const double* LT0, const doub
     if (n64 > 0)
       hipLaunchKernelGGL((hinv_trail<64, 16>), dim3(unsigned(n64)), dim3(256), 0, st, w.A, w.R, LT0, LT, d, q);
   }
+  return true;
 }
 
 }  // namespace
@@ -896,8 +904,9 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
       // from super-panels p - 1 (whose trail B left them out) and p
       const int p0 = p >= 1 ? s0 - KS : s0;
       const double* LT0 = p >= 1 ? w.LT + size_t((p - 1) % NPANEL) * KS * di : LTw;
-      launch_trail(s, w, LT0, LTw, di, TrailSpec{s0, s1, s1, 0, s1, s2 - s1, s1, s2 - s1, p0}, false,
-                   by_launch ? ctx->chain[p % NPANEL] : nullptr);
+      if (!launch_trail(s, w, LT0, LTw, di, TrailSpec{s0, s1, s1, 0, s1, s2 - s1, s1, s2 - s1, p0}, false,
+                        by_launch ? ctx->chain[p % NPANEL] : nullptr))
+        return GPTQ_E_HIP;
       if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
       if (ctx && !by_launch && hipEventRecord(ctx->chain[p % NPANEL], s) != hipSuccess) return GPTQ_E_HIP;
       // trail B: A at and beyond s3 (lower triangle), R rows from s3. It
