@@ -10,10 +10,11 @@
 //    (4 waves, 2x2, each wave 128x128 = 4x4 MFMA 32x32x16 f16 tiles) owns one
 //    tile for one contiguous token range (split-K).
 //  * X is copied from HBM straight into LDS (global_load_lds, 16 bytes per
-//    lane) in its natural token-major layout, double buffered so the loads of
-//    step k+1 overlap the MFMAs of step k; no registers or VALU work are
-//    spent on staging. MFMA operands need 8 consecutive tokens of one channel
-//    per lane: they are read with the gfx950 transposing LDS read
+//    lane) in its natural token-major layout, in four stages of 32 tokens:
+//    the loads of step k+3 are in flight while step k's MFMAs run; no
+//    registers or VALU work are spent on staging. MFMA operands need 8
+//    consecutive tokens of one channel per lane: they are read with the
+//    gfx950 transposing LDS read
 //    (ds_read_b64_tr_b16), two per fragment, at per-lane base + immediate
 //    offsets. Ragged tokens or channels take a checked register path into
 //    the same layout.
