@@ -36,7 +36,7 @@ def gpu_tensor(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def check_quant(q, ref, bits, rows=None, tie=1e-3):
+def check_quant(q, ref, bits, rows=None, tie=1e-3, min_match=0.999, max_flip_rows=1.0, post_rtol=5e-2):
     codes = q.codes.cpu().numpy()
     scales = q.scales.cpu().numpy()
     zeros = q.zeros.cpu().numpy()
@@ -69,11 +69,14 @@ def check_quant(q, ref, bits, rows=None, tie=1e-3):
     n_div = int(np.sum(first < d_col))
     say(f"  codes match {match:.6f}; rows with a near-tie flip {n_div}/{len(first)}; "
         f"entries before each row's first flip {float(np.mean(np.minimum(first, d_col))) / d_col:.4f}")
-    assert match >= 0.999, f"codes match {match}"
+    assert match >= min_match, f"codes match {match}"
+    assert n_div <= max(1, max_flip_rows * len(first)), f"{n_div} of {len(first)} rows flipped"
     same = (np.arange(ng)[None, :] * g) < first[:, None]
     assert np.allclose(scales[same], ref["scales"][same], rtol=1e-3, atol=0)
     assert np.all(zeros[same] == ref["zeros"][same])
-    assert np.all(scales > 0) and np.allclose(scales, ref["scales"], rtol=5e-2)
+    assert np.all(scales > 0)
+    if post_rtol is not None:
+        assert np.allclose(scales, ref["scales"], rtol=post_rtol)
     # packing of the GPU's own codes is bit-exact
     assert np.array_equal(packed, O.pack(codes, bits))
     lref = float(np.sum(ref["row_loss"]))
@@ -344,6 +347,60 @@ def test_identity_hessian_is_rtn_bit_exact(gpu, bits, group):
     assert np.array_equal(q.codes.cpu().numpy(), ref["codes"])
     assert np.array_equal(q.zeros.cpu().numpy(), ref["zeros"].astype(np.int32))
     assert np.allclose(q.scales.cpu().numpy(), ref["scales"], rtol=1e-7)
+
+
+def _random_layers(n=24, seed=20261203):
+    """Seeded random layers: shape, width, group (whole row, or a multiple of
+    16 that divides or is divided by the 128-column block), grid, and the
+    dtypes of the weights and activations; tokens from half to three times
+    the width (the Hessian is rank-deficient below the width)."""
+    r = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        d_row, d_col = int(r.integers(1, 300)), int(r.integers(1, 700))
+        bits = int(r.choice([2, 3, 4, 8]))
+        group = int(r.choice([-1, 16, 32, 64, 128, 256, 384, 512]))
+        sym = bool(r.integers(0, 2))
+        wdt = np.float16 if r.integers(0, 2) else np.float32
+        xdt = np.float16 if r.integers(0, 2) else np.float32
+        n_tok = int(r.integers(max(1, d_col // 2), 3 * d_col + 2))
+        out.append((d_row, d_col, bits, group, sym, wdt, xdt, n_tok))
+    return out
+
+
+RANDOM_LAYERS = _random_layers()
+
+
+@pytest.mark.parametrize("case", range(len(RANDOM_LAYERS)))
+def test_layer_path_random_shapes(gpu, case):
+    """Hessian and factor from seeded activations against the oracle's own
+    chain, then the sweep on the oracle's factor against the oracle's sweep
+    (same near-tie criteria as the fixed cases)."""
+    d_row, d_col, bits, group, sym, wdt, xdt, n_tok = RANDOM_LAYERS[case]
+    say("random layer", case, d_row, d_col, bits, group, "sym" if sym else "asym", wdt.__name__, xdt.__name__, n_tok)
+    X = make_x(n_tok, d_col, xdt, 1000 + case)
+    W = (0.02 * np.random.default_rng(2000 + case).standard_normal((d_row, d_col))).astype(wdt)
+    H = gpu.gptq_hessian_accumulate(gpu_tensor(X))
+    hv = gpu.gptq_prepare_hinv(H, 0.01)
+    torch.cuda.synchronize()
+    Href = O.hessian(X)
+    assert rel_fro(H.cpu().numpy(), Href) < 1e-4
+    Uref, lam = O.prepare_hinv(Href, 0.01)
+    assert int(hv.info.item()) == 0
+    # fp32 H, fp64 factor: U's error is H's rounding times the damped conditioning
+    assert rel_fro(hv.U.cpu().numpy(), Uref) < 5e-3
+    assert abs(float(hv.lam.item()) - lam) <= 1e-4 * lam
+    U32 = Uref.astype(np.float32)
+    q = gpu.gptq_quantize_layer(gpu_tensor(W), gpu_tensor(U32), bits, group, 128, symmetric=sym)
+    torch.cuda.synchronize()
+    ref = O.quantize_layer(W, U32, bits, group, 128, decide=np.float32, symmetric=sym)
+    # A row that takes the other side of a near-tie has its own valid
+    # continuation. At 8 bits that continuation differs in most later codes,
+    # and a small group's scale after it follows the row's own values, so
+    # neither the share of equal codes nor those scales' closeness says much
+    # there; the share of rows that diverge at all is bounded instead, and
+    # the later scales must be positive.
+    check_quant(q, ref, bits, min_match=0.99 if bits == 8 else 0.999, max_flip_rows=0.05, post_rtol=None)
 
 
 SYM_CASES = [
