@@ -572,11 +572,12 @@ hinv_step(const StepArgs g, int32_t* __restrict__ info) {
 // tiles left of s0, since X_Pc is zero for c >= s0), accumulating both in the
 // same registers: K = (s0 - p0) + (s1 - s0), in the order P then S.
 // Each wave owns a (T/2) x (T/2) quarter (T = 128: 16 independent MFMA
-// chains; T = 64, used when big tiles would leave CUs idle: 4 chains). The
-// operands (L_S column-major in LT; X_S as rows s0.. of R) pass through LDS
-// in chunks of 16 k; the next chunk's loads are in flight while the current
-// one is multiplied. The accumulators start from the old tile, so it is read
-// once and written once.
+// chains; T = 64, used when big tiles would leave CUs idle: 4 chains; T = 32,
+// for the latency-bound look-ahead update: 1 chain). The operands (L_S
+// column-major in LT; X_S as rows s0.. of R) pass through LDS in chunks of TK
+// k (16 for the bulk update, 32 for the look-ahead); the next chunk's loads
+// are in flight while the current one is multiplied. The accumulators start
+// from the old tile, so it is read once and written once.
 struct TrailSpec {
   int s0, s1;     // the super-panel whose columns are applied (K = s1 - s0)
   int ra0, naR;   // A part: first row (and, if tri, first column), tile rows
