@@ -169,7 +169,8 @@ def prepare_hinv(H: np.ndarray, damp: float):
 # --------------------------------------------------------------------------
 # Quantizer
 # --------------------------------------------------------------------------
-def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False, symmetric: bool = False):
+def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False, symmetric: bool = False,
+                 flip=None):
     """Per-row min-max scale and integer zero of a group of columns.
 
     aiqz.cc, section 分组方案: scale = (max - min)/(2^bits - 1) and the zero
@@ -190,6 +191,11 @@ def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False
     as unsigned codes, the signed value plus 2^(b-1), so the zero point is
     the fixed code 2^(b-1). An all-zero group uses max|x| = 1. The zero is
     not a rounding decision here, so its margin is reported as 0.5.
+
+    ``flip`` (optional boolean [rows]): in the rows it marks, the zero point
+    takes the other rounding of -xmin/s, the integer on the other side of
+    the nearest rounding boundary. Parity tests use this to follow a row
+    whose float32 history crossed a near-tie; it is not part of the method.
     """
     if symmetric:
         qs = (1 << (bits - 1)) - 1
@@ -200,6 +206,8 @@ def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False
         else:
             s = (amax.astype(decide) / decide(qs)).astype(F64)
         z = np.full(s.shape, float(1 << (bits - 1)))
+        if flip is not None and np.any(flip):
+            raise ValueError("the symmetric grid's zero point is fixed, not a rounding decision")
         if with_margin:
             return s.astype(F64), z, np.full(s.shape, 0.5)
         return s.astype(F64), z
@@ -217,16 +225,28 @@ def group_params(x: np.ndarray, bits: int, decide=F64, with_margin: bool = False
         t = ((-xmin.astype(decide)) / s32).astype(F64)
         s = s32.astype(F64)
     z = np.rint(t)
+    margin = 0.5 - np.abs(t - z)
+    if flip is not None:
+        z = np.where(flip, _other_rounding(t, z), z)
     if with_margin:
-        return s.astype(F64), z.astype(F64), 0.5 - np.abs(t - z)
+        return s.astype(F64), z.astype(F64), margin
     return s.astype(F64), z.astype(F64)
 
 
-def quantize_codes(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decide=F64, with_margin: bool = False):
+def _other_rounding(t, n):
+    """The integer on the other side of the rounding boundary nearest to t,
+    where n = rint(t): n + 1 if t lies above n, else n - 1."""
+    return np.where(t > n, n + 1.0, n - 1.0)
+
+
+def quantize_codes(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decide=F64, with_margin: bool = False,
+                   flip=None):
     """code = clamp(rint(w/s) + z, 0, 2^b - 1) (astro-blog survey, 1.2).
 
     With ``with_margin`` it also returns how far w/s lay from the nearest
-    rounding boundary, in grid steps (0 = an exact tie).
+    rounding boundary, in grid steps (0 = an exact tie). ``flip`` (optional
+    boolean, shaped like w) takes the other rounding of w/s where set (see
+    ``group_params``; a test device, not part of the method).
     """
     maxq = (1 << bits) - 1
     if decide == F64:
@@ -234,9 +254,12 @@ def quantize_codes(w: np.ndarray, s: np.ndarray, z: np.ndarray, bits: int, decid
     else:
         t = (w.astype(decide) / s.astype(decide)).astype(F64)
     q = np.rint(t)
+    margin = 0.5 - np.abs(t - q)
+    if flip is not None:
+        q = np.where(flip, _other_rounding(t, q), q)
     c = np.clip(q + z, 0, maxq)
     if with_margin:
-        return c, 0.5 - np.abs(t - q)
+        return c, margin
     return c
 
 
@@ -285,6 +308,7 @@ def quantize_layer(
     block: int = 128,
     decide=F64,
     symmetric: bool = False,
+    flips=(),
 ):
     """GPTQ sweep of one layer, columns in natural order.
 
@@ -310,6 +334,12 @@ def quantize_layer(
     default; float32 reproduces the decision of a float32 implementation
     given the same inputs). ``symmetric`` selects the symmetric grid of
     ``group_params``.
+
+    ``flips`` (a test device, empty for the method itself): (row, "code",
+    column) or (row, "zero", group) entries; at each, that row's decision
+    takes the other rounding, and the sweep continues from there exactly as
+    the method does. The margins returned are those of the decisions as
+    computed, before any flip.
     """
     W = np.array(W, dtype=F64, copy=True)
     U = np.asarray(U, dtype=F64)
@@ -331,9 +361,19 @@ def quantize_layer(
     row_loss = np.zeros(d_row)
     code_margin = np.zeros((d_row, d_col))
     zero_margin = np.zeros((d_row, n_groups))
+    code_flip, zero_flip = {}, {}
+    for r, kind, idx in flips:
+        if not (0 <= r < d_row):
+            raise ValueError(f"flip row {r} out of range")
+        if kind == "code" and 0 <= idx < d_col:
+            code_flip.setdefault(idx, np.zeros(d_row, dtype=bool))[r] = True
+        elif kind == "zero" and 0 <= idx < n_groups:
+            zero_flip.setdefault(idx, np.zeros(d_row, dtype=bool))[r] = True
+        else:
+            raise ValueError(f"bad flip {(r, kind, idx)}")
 
     if group_size == -1 and d_col:
-        s, z, zm = group_params(W, bits, decide, with_margin=True, symmetric=symmetric)
+        s, z, zm = group_params(W, bits, decide, with_margin=True, symmetric=symmetric, flip=zero_flip.get(0))
         scales[:, 0], zeros[:, 0], zero_margin[:, 0] = s, z, zm
 
     for i1 in range(0, d_col, block):
@@ -343,11 +383,12 @@ def quantize_layer(
             if group_size != -1 and q % group_size == 0:
                 k = q // group_size
                 s, z, zm = group_params(
-                    W[:, q : min(q + group_size, d_col)], bits, decide, with_margin=True, symmetric=symmetric
+                    W[:, q : min(q + group_size, d_col)], bits, decide, with_margin=True, symmetric=symmetric,
+                    flip=zero_flip.get(k),
                 )
                 scales[:, k], zeros[:, k], zero_margin[:, k] = s, z, zm
             w = W[:, q]
-            c, code_margin[:, q] = quantize_codes(w, s, z, bits, decide, with_margin=True)
+            c, code_margin[:, q] = quantize_codes(w, s, z, bits, decide, with_margin=True, flip=code_flip.get(q))
             what = s * (c - z)
             err = w - what
             d = U[q, q]

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle.gptq_oracle as O
+from tests.parity import rerun_for
 from tests.test_gpu_parity import DEV, check_quant, gpu_tensor, say
 
 pytestmark = pytest.mark.gpu
@@ -152,7 +153,7 @@ def test_act_order_layer_parity(gpu, d_row, d_col, bits, group, wdt):
     assert int(hv.info.item()) == 0 and int(i1.item()) == 0 and int(i2.item()) == 0 and int(i3.item()) == 0
     ref = O.quantize_layer_act_order(W, H.astype(np.float64), bits, group, 128, damp, decide=np.float32)
     assert np.array_equal(perm.cpu().numpy(), ref["perm"])
-    check_quant(q, ref, bits)
+    check_quant(q, ref, bits, rerun_for(W[:, ref["perm"]], ref["U"], bits, group))
     assert np.array_equal(codes_orig.cpu().numpy(), q.codes.cpu().numpy()[:, ref["perm"].argsort()])
 
 

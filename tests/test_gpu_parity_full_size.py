@@ -7,6 +7,9 @@ the benchmark times (needs an MI355X).
   library receives it, and are compared in full.
 * Sweep: the GPU quantizes the whole weight matrix with the oracle's factor.
   The oracle sweeps a seeded sample of 256 rows; rows are independent given U.
+  Each sampled row must equal the oracle's row or its continuation through
+  near-tie decisions (tests/parity.py), once with the decisions taken in
+  float32 (the kernel's precision) and once in float64.
 
 No value from the HIP path is fed to the oracle.
 """
@@ -16,6 +19,7 @@ import pytest
 import torch
 
 import oracle.gptq_oracle as O
+from tests.parity import rerun_for
 from tests.test_gpu_parity import DEV, check_quant, gpu_tensor, rel_fro, say
 from workload import CONFIGS, activation_chunks, weights
 
@@ -108,9 +112,12 @@ def test_full_size_layer(gpu, name):
     rows = np.sort(np.random.default_rng(7).choice(cfg.d_row, N_SAMPLE_ROWS, replace=False))
     rows[-1] = cfg.d_row - 1
     rows = np.unique(rows)
-    ref = O.quantize_layer(W[rows], U32.astype(np.float64), cfg.bits, cfg.group_size, cfg.block, decide=np.float32)
-    m = check_quant(q, ref, cfg.bits, rows=rows)
-    say(f"{name}: sampled rows {len(rows)}, codes match {m:.6f}")
+    U64 = U32.astype(np.float64)
+    for decide in (np.float32, np.float64):
+        # decisions in the kernel's precision, then in the oracle's own
+        ref = O.quantize_layer(W[rows], U64, cfg.bits, cfg.group_size, cfg.block, decide=decide)
+        check_quant(q, ref, cfg.bits, rerun_for(W[rows], U64, cfg.bits, cfg.group_size, cfg.block, decide=decide),
+                    rows=rows, label=f"{name}, {decide.__name__} decisions")
     # outputs of every row are on the grid: zeros within range, scales positive
     zeros = q.zeros.cpu().numpy()
     assert zeros.min() >= 0 and zeros.max() <= (1 << cfg.bits) - 1
@@ -144,7 +151,9 @@ def test_full_size_act_order_layer(gpu):
     rows = np.sort(np.random.default_rng(8).choice(cfg.d_row, N_SAMPLE_ROWS, replace=False))
     rows[-1] = cfg.d_row - 1
     rows = np.unique(rows)
-    ref = O.quantize_layer(W[rows][:, p], U_ref.astype(np.float32).astype(np.float64), cfg.bits, cfg.group_size,
-                           cfg.block, decide=np.float32)
-    m = check_quant(q, ref, cfg.bits, rows=rows)
-    say(f"act-order sampled rows {len(rows)}, codes match {m:.6f}")
+    Wp_rows = W[rows][:, p]
+    Up = U_ref.astype(np.float32).astype(np.float64)
+    for decide in (np.float32, np.float64):
+        ref = O.quantize_layer(Wp_rows, Up, cfg.bits, cfg.group_size, cfg.block, decide=decide)
+        check_quant(q, ref, cfg.bits, rerun_for(Wp_rows, Up, cfg.bits, cfg.group_size, cfg.block, decide=decide),
+                    rows=rows, label=f"act-order, {decide.__name__} decisions")
