@@ -4,14 +4,17 @@ One step is the whole layer path on device-resident inputs:
   H = 2 X^T X (gptq_hessian_accumulate), U = chol((H + lambda I)^-1)
   (gptq_prepare_hinv), and the column sweep with packing and loss
   (gptq_quantize_layer).
-Default workload: the 4096 x 4096 fp16 attention-projection layer with
-128 x 2048 = 262144 fp16 calibration tokens, 4-bit, group 128, damp 0.01,
-B = 128 (seeded synthetic inputs standing in for C4 activations).
+Default workload: the 175B-class layer W 49152 x 12288 fp16, 3-bit, group
+128, with 128 x 2048 = 262144 fp16 calibration tokens of width 12288, damp
+0.01, B = 128 (seeded synthetic inputs standing in for C4 activations and
+real weights). This is the largest layer one GPU quantizes on its own.
 
 Prints one JSON line. `value` is weight columns quantized per second for
 the whole layer path (d_col / step time); per-stage times, the Hessian
-TFLOP/s, the roofline of the dominant stage and the float64 oracle's rate
-on this machine's CPU cores are reported beside it.
+TFLOP/s, each stage against its roofline (the dominant stage's as
+`roofline`), the same path on the 4096 x 4096 attention-projection layer,
+and the float64 oracle's rate on this machine's CPU cores are reported
+beside it.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 """
@@ -54,22 +57,26 @@ def upload_activations(cfg, torch, dev):
     return X
 
 
-def hessian_traffic_bytes():
-    """HBM bytes per Hessian-stage call from the committed counter summary.
+def counter_traffic_bytes(profile: str, source: str, tag: str):
+    """HBM bytes per call of one stage from a committed counter summary.
 
-    profiles/hessian_syrk_attn4096_counters.md holds FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch, summed over the stage's two kernels), the
-    copy-calibration scales and the SHA-256 of the kernel source they were
-    taken with. Returns None when that source has changed since.
+    The summary under profiles/ holds a line
+    `bench-traffic[<tag>]: source_sha256=... fetch_kib=... write_kib=...
+    fetch_scale=... write_scale=...` with FETCH_SIZE and WRITE_SIZE (KiB
+    per call, summed over the stage's kernels), the copy-calibration
+    scales and the SHA-256 of the kernel source they were taken with.
+    Returns None when that source has changed since (the counters no
+    longer describe the kernel) or the line is missing.
     """
     import hashlib
     import re
 
-    path = os.path.join(ROOT, "profiles", "hessian_syrk_attn4096_counters.md")
-    src = os.path.join(ROOT, "post_weight_quantization_17_amd", "csrc", "hessian.hip")
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "post_weight_quantization_17_amd", "csrc", source)
     try:
         text = open(path).read()
-        m = re.search(r"bench-traffic: source_sha256=(\w+) fetch_kib=(\S+) write_kib=(\S+) fetch_scale=(\S+) write_scale=(\S+)", text)
+        m = re.search(rf"bench-traffic\[{re.escape(tag)}\]: source_sha256=(\w+) fetch_kib=(\S+) write_kib=(\S+) "
+                      rf"fetch_scale=(\S+) write_scale=(\S+)", text)
         if not m or hashlib.sha256(open(src, "rb").read()).hexdigest() != m.group(1):
             return None
         fk, wk, fs, ws = (float(m.group(i)) for i in range(2, 6))
@@ -78,55 +85,77 @@ def hessian_traffic_bytes():
         return None
 
 
-def cpu_baseline(cfg, budget_rows=128, budget_tokens=16384):
-    """The float64 oracle timed on a bounded sample of the same layer.
+def cpu_baseline(cfg, budget_rows=256, budget_tokens=8192, budget_width=6144):
+    """The float64 oracle timed on a bounded sample of the same layer, on
+    this machine's host cores (BLAS threads set to the cores this process
+    may run on).
 
-    Sample: the Hessian of the first `budget_tokens` tokens (time scaled by
-    n_tokens / budget_tokens, the cost being linear in tokens), the damped
-    factor of that Hessian at full width, and the sweep of `budget_rows`
-    rows (time scaled by d_row / budget_rows; rows are independent).
+    Sample (rows are independent given U, and the Hessian's cost is linear
+    in tokens): the Hessian of the first `budget_tokens` tokens, its time
+    scaled by n_tokens / budget_tokens; the damped factor (route A as the
+    oracle states it) at full width up to `budget_width`, else of the
+    leading budget_width x budget_width block of that Hessian with its time
+    scaled by (d / budget_width)^3 (dense Cholesky and inversion cost d^3);
+    the plain column sweep of a fixed seeded subset of `budget_rows` rows
+    with the full-width factor's shape, its time scaled by d_row /
+    budget_rows. The whole oracle runs when the layer is that small.
     """
     import oracle.gptq_oracle as O
     from workload import activation_chunks, weights
 
+    cores = len(os.sched_getaffinity(0))
+    blas_threads = None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    chunks = []
-    got = 0
+        limiter = threadpool_limits(cores)
+        blas_threads = max([p.get("num_threads", 0) for p in threadpool_info()] or [0]) or None
+    except Exception:  # pragma: no cover - threadpoolctl is part of the image
+        limiter = None
+    chunks, got = [], 0
     for ch in activation_chunks(cfg, threads=4):
         chunks.append(ch)
         got += ch.shape[0]
         if got >= budget_tokens:
             break
     Xs = np.concatenate(chunks)[:budget_tokens]
-    rows = np.arange(min(budget_rows, cfg.d_row))
+    n_rows = min(budget_rows, cfg.d_row)
+    rows = np.sort(np.random.default_rng(0).choice(cfg.d_row, n_rows, replace=False))
     Ws = weights(cfg, rows=rows)
+    fw = min(cfg.d_col, budget_width)
     t0 = time.perf_counter()
     H = O.hessian([Xs[i : i + 4096] for i in range(0, len(Xs), 4096)])
     t1 = time.perf_counter()
-    U, _ = O.prepare_hinv(H, cfg.damp)
+    O.prepare_hinv(H[:fw, :fw], cfg.damp)
     t2 = time.perf_counter()
+    # the sweep needs a factor of full width: the Hessian's diagonal part
+    # gives one at O(d) cost (the sweep's own cost does not depend on U's values)
+    U = np.diag(1.0 / np.sqrt(np.diag(H) * (1 + cfg.damp)))
+    t2b = time.perf_counter()
     O.quantize_layer(Ws, U, cfg.bits, cfg.group_size, cfg.block)
     t3 = time.perf_counter()
+    if limiter is not None:
+        limiter.restore_original_limits()
     t_h = (t1 - t0) * cfg.n_tokens / len(Xs)
-    t_u = t2 - t1
-    t_q = (t3 - t2) * cfg.d_row / len(rows)
+    t_u = (t2 - t1) * (cfg.d_col / fw) ** 3
+    t_q = (t3 - t2b) * cfg.d_row / n_rows
     total = t_h + t_u + t_q
+    full = len(Xs) == cfg.n_tokens and n_rows == cfg.d_row and fw == cfg.d_col
     return {
         "value": cfg.d_col / total,
         "unit": "weight-cols/s",
         "cores": int(cores),
+        "blas_threads": blas_threads,
         "kind": "oracle",
         "sample": (
-            f"float64 numpy oracle: Hessian of {len(Xs)} of {cfg.n_tokens} tokens (x{cfg.n_tokens / len(Xs):.0f}), "
-            f"full-width damped factor, sweep of {len(rows)} of {cfg.d_row} rows (x{cfg.d_row / len(rows):.0f}); "
-            f"measured {t3 - t0:.1f} s, extrapolated layer time {total:.1f} s"
+            "float64 numpy oracle, whole layer" if full else
+            f"float64 numpy oracle: Hessian of {len(Xs)} of {cfg.n_tokens} tokens (time x{cfg.n_tokens / len(Xs):.0f}), "
+            f"damped factor at width {fw} of {cfg.d_col} (time x{(cfg.d_col / fw) ** 3:.1f}), plain sweep of "
+            f"{n_rows} seeded rows of {cfg.d_row} (time x{cfg.d_row / n_rows:.0f}); measured {t3 - t0:.1f} s on "
+            f"{cores} cores, extrapolated layer time {total:.1f} s"
         ),
-        "stage_s": {"hessian": t_h, "hinv": t_u, "quantize": t_q},
+        "stage_s": {"hessian": t_h, "prepare_hinv": t_u, "quantize_layer": t_q},
+        "measured_s": t3 - t0,
     }
 
 
@@ -342,15 +371,129 @@ def pipeline_measure(g, torch, X, W, cfg, steps=2):
     }
 
 
+def layer_leg(g, torch, cfg, X, W, steps, warmup):
+    """The layer path (Hessian, factor, sweep) on device-resident X and W:
+    `warmup` untimed steps (the first event-timed per stage and reported as
+    the cold step), then `steps` steps, each stage bracketed by HIP events
+    on torch's current stream, which is the stream every call enqueues on.
+    Returns the times and the last step's outputs."""
+    dev = X.device
+    d, n = cfg.d_col, cfg.n_tokens
+    ws_h = torch.empty(g.gptq_hessian_workspace_size(n, d, X.dtype), dtype=torch.uint8, device=dev)
+    ws_u = torch.empty(g.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(
+        g.gptq_quantize_layer_workspace_size(cfg.d_row, d, cfg.bits, cfg.group_size, cfg.block), dtype=torch.uint8,
+        device=dev)
+    H = torch.empty((d, d), dtype=torch.float32, device=dev)
+    hv = g.Hinv(
+        torch.empty((d, d), dtype=torch.float32, device=dev),
+        torch.empty((), dtype=torch.float32, device=dev),
+        torch.empty((), dtype=torch.int32, device=dev),
+    )
+    eye = torch.eye(d, dtype=torch.float32, device=dev)
+    q = g.gptq_quantize_layer(W, eye, cfg.bits, cfg.group_size, cfg.block, ws=ws_q)  # allocates the outputs once
+    del eye
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        g.gptq_hessian_accumulate(X, H=H, ws=ws_h)
+        if ev:
+            ev[1].record()
+        g.gptq_prepare_hinv(H, cfg.damp, ws=ws_u, out=hv)
+        if ev:
+            ev[2].record()
+        g.gptq_quantize_layer(W, hv.U, cfg.bits, cfg.group_size, cfg.block, ws=ws_q, out=q)
+        if ev:
+            ev[3].record()
+
+    # The first warm-up step is the cold call (code objects load, the factor's
+    # auxiliary stream is created); it is event-timed and reported apart.
+    cold = None
+    for w in range(warmup):
+        if w == 0:
+            cev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            step(cev)
+            torch.cuda.synchronize()
+            cold = {
+                "total": cev[0].elapsed_time(cev[3]),
+                "hessian": cev[0].elapsed_time(cev[1]),
+                "prepare_hinv": cev[1].elapsed_time(cev[2]),
+                "quantize_layer": cev[2].elapsed_time(cev[3]),
+            }
+        else:
+            step()
+    torch.cuda.synchronize()
+    if int(hv.info.item()) != 0:
+        raise RuntimeError(f"factorization failed: info={int(hv.info.item())}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        step(evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(end) / steps
+    stages = {
+        "hessian": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+        "prepare_hinv": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+        "quantize_layer": float(np.mean([e[2].elapsed_time(e[3]) for e in evs])),
+    }
+    median_ms = float(np.median([e[0].elapsed_time(e[3]) for e in evs]))
+    log(f"bench: {cfg.name}: {steps} steps in {wall:.3f} s wall; per step {ms:.3f} ms "
+        f"(H {stages['hessian']:.3f}, U {stages['prepare_hinv']:.3f}, Q {stages['quantize_layer']:.3f})")
+    return dict(ms=ms, median_ms=median_ms, stages=stages, cold=cold, wall_s=wall, H=H, hv=hv, q=q, ws_u=ws_u,
+                ws_q=ws_q)
+
+
+def stage_rooflines(cfg, stages):
+    """Each stage against the roofline that bounds it, on algorithmic work:
+    the Hessian's triangle N d (d + 1) flops on the fp16 MFMA peak, the
+    factor's 2 d^3 / 3 flops (route B) on the fp64 peak, the sweep's
+    deferred-update flops sum over blocks of 2 d_row B (d_col - i2) on the
+    fp32 peak. `traffic` is HBM bytes per call from the committed counter
+    summary of that workload, or null when none matches the current source."""
+    d, n = cfg.d_col, cfg.n_tokens
+    prof = f"{cfg.name}_counters.md"
+    syrk_flops = float(n) * d * (d + 1)
+    chol_flops = 2.0 * d**3 / 3.0
+    trail_flops = float(sum(2.0 * cfg.d_row * cfg.block * (d - i2) for i2 in range(cfg.block, d, cfg.block)))
+
+    def rl(kernel, flops, ms, peak, dtype, source, tag):
+        achieved = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "dtype": dtype, "kernel": kernel, "achieved": achieved, "peak": peak / 1e12,
+                "unit": "TFLOP/s", "frac": achieved * 1e12 / peak,
+                "traffic": counter_traffic_bytes(prof, source, tag), "traffic_unit": "bytes",
+                "per_launch_flops": flops, "launch_ms": ms}
+
+    return {
+        "hessian": rl("syrk_f16_lds + syrk_reduce (one gptq_hessian_accumulate call)", syrk_flops,
+                      stages["hessian"], PEAK_FP16_MFMA, "f16 in, f32 accumulate", "hessian.hip", "hessian"),
+        "prepare_hinv": rl("hinv_* chain (one gptq_prepare_hinv call; route B, fp64)", chol_flops,
+                           stages["prepare_hinv"], PEAK_FP64_MFMA, "f64", "hinv.hip", "prepare_hinv"),
+        "quantize_layer": rl("gptq_sweep + loss_final (one gptq_quantize_layer call); flops of the deferred update "
+                             "only", trail_flops, stages["quantize_layer"], PEAK_FP32_MFMA, "f32", "quantize.hip",
+                             "quantize_layer"),
+    }
+
+
+SECOND_LAYER = "attn_proj_4096x4096_4bit_g128"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="attn_proj_4096x4096_4bit_g128")
+    ap.add_argument("--config", default="opt175b_49152x12288_3bit_g128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layer-only", action="store_true",
-                    help="time only the layer path (no act-order, packed-product or pipeline legs)")
+                    help="time only the layer path of --config (no act-order, packed-product, second-layer or "
+                         "pipeline legs)")
     ap.add_argument(
         "--copy-calibration",
         action="store_true",
@@ -389,88 +532,12 @@ def main():
     torch.cuda.synchronize()
     log(f"bench: inputs resident in HBM after {time.perf_counter() - t0:.1f} s")
 
+    leg = layer_leg(g, torch, cfg, X, W, args.steps, args.warmup)
+    ms, stages = leg["ms"], leg["stages"]
     d, n = cfg.d_col, cfg.n_tokens
-    ws_h = torch.empty(g.gptq_hessian_workspace_size(n, d, X.dtype), dtype=torch.uint8, device=dev)
-    ws_u = torch.empty(g.gptq_prepare_hinv_workspace_size(d), dtype=torch.uint8, device=dev)
-    ws_q = torch.empty(
-        g.gptq_quantize_layer_workspace_size(cfg.d_row, d, cfg.bits, cfg.group_size, cfg.block), dtype=torch.uint8, device=dev
-    )
-    H = torch.empty((d, d), dtype=torch.float32, device=dev)
-    hv = g.Hinv(
-        torch.empty((d, d), dtype=torch.float32, device=dev),
-        torch.empty((), dtype=torch.float32, device=dev),
-        torch.empty((), dtype=torch.int32, device=dev),
-    )
-    eye = torch.eye(d, dtype=torch.float32, device=dev)
-    q = g.gptq_quantize_layer(W, eye, cfg.bits, cfg.group_size, cfg.block, ws=ws_q)  # allocates the outputs once
-    del eye
-
-    def step(ev=None):
-        if ev:
-            ev[0].record()
-        g.gptq_hessian_accumulate(X, H=H, ws=ws_h)
-        if ev:
-            ev[1].record()
-        g.gptq_prepare_hinv(H, cfg.damp, ws=ws_u, out=hv)
-        if ev:
-            ev[2].record()
-        g.gptq_quantize_layer(W, hv.U, cfg.bits, cfg.group_size, cfg.block, ws=ws_q, out=q)
-        if ev:
-            ev[3].record()
-
-    # The first warm-up step is the cold call (code objects load, the factor's
-    # auxiliary stream is created); it is event-timed and reported apart.
-    cold = None
-    for w in range(args.warmup):
-        if w == 0:
-            cev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            step(cev)
-            torch.cuda.synchronize()
-            cold = {
-                "total": cev[0].elapsed_time(cev[3]),
-                "hessian": cev[0].elapsed_time(cev[1]),
-                "prepare_hinv": cev[1].elapsed_time(cev[2]),
-                "quantize_layer": cev[2].elapsed_time(cev[3]),
-            }
-        else:
-            step()
-    torch.cuda.synchronize()
-    if int(hv.info.item()) != 0:
-        raise RuntimeError(f"factorization failed: info={int(hv.info.item())}")
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
-    for k in range(args.steps):
-        step(evs[k])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = start.elapsed_time(end) / args.steps
-    t_h = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    t_u = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    t_q = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    median_ms = float(np.median([e[0].elapsed_time(e[3]) for e in evs]))
-    log(f"bench: {args.steps} steps in {wall:.3f} s wall; per step {ms:.3f} ms (H {t_h:.3f}, U {t_u:.3f}, Q {t_q:.3f})")
-
-    syrk_flops = float(n) * d * (d + 1)
-    syrk_tflops = syrk_flops / (t_h * 1e-3) / 1e12
-    trail_flops = float(sum(2.0 * cfg.d_row * cfg.block * (d - i2) for i2 in range(cfg.block, d, cfg.block)))
-    chol_flops = 2.0 * d**3 / 3.0
-    traffic = hessian_traffic_bytes() if cfg.name == "attn_proj_4096x4096_4bit_g128" else None
-    roofline = {
-        "bound": "mfma",
-        "kernel": "Hessian stage: syrk_f16_lds + syrk_reduce (one gptq_hessian_accumulate call)",
-        "achieved": syrk_tflops,
-        "peak": PEAK_FP16_MFMA / 1e12,
-        "unit": "TFLOP/s",
-        "frac": syrk_tflops * 1e12 / PEAK_FP16_MFMA,
-        "traffic": traffic,
-        "traffic_unit": "bytes",
-        "per_launch_flops": syrk_flops,
-    }
+    rls = stage_rooflines(cfg, stages)
+    dominant = max(stages, key=stages.get)
+    syrk_tflops = rls["hessian"]["achieved"]
     out = {
         "metric": METRIC,
         "value": d / (ms * 1e-3),
@@ -494,28 +561,50 @@ def main():
             "block": cfg.block,
             "damp": cfg.damp,
         },
-        "stages_ms": {"hessian": t_h, "prepare_hinv": t_u, "quantize_layer": t_q},
-        "quantize_layer_ms": t_q,
-        "median_step_ms": median_ms,
-        "cold_step_ms": cold,
-        "quantize_weight_cols_per_s": d / (t_q * 1e-3),
+        "stages_ms": stages,
+        "layer_ms": ms,
+        "quantize_layer_ms": stages["quantize_layer"],
+        "median_step_ms": leg["median_ms"],
+        "cold_step_ms": leg["cold"],
+        "quantize_weight_cols_per_s": d / (stages["quantize_layer"] * 1e-3),
+        "weights_per_s": cfg.d_row * d / (ms * 1e-3),
         "hessian_tflops": syrk_tflops,
-        "hessian_pct_fp16_peak": 100.0 * syrk_tflops * 1e12 / PEAK_FP16_MFMA,
-        "prepare_hinv_tflops_fp64": chol_flops / (t_u * 1e-3) / 1e12,
-        "quantize_trailing_tflops_lower_bound": trail_flops / (t_q * 1e-3) / 1e12,
-        "roofline": roofline,
+        "hessian_pct_fp16_peak": 100.0 * rls["hessian"]["frac"],
+        "prepare_hinv_tflops_fp64": rls["prepare_hinv"]["achieved"],
+        "quantize_trailing_tflops_lower_bound": rls["quantize_layer"]["achieved"],
+        "roofline": dict(rls[dominant], stage=dominant),
+        "stage_rooflines": rls,
+        "roofline_floor_ms": float(sum(r["per_launch_flops"] / (r["peak"] * 1e12) * 1e3 for r in rls.values())),
         "cpu_baseline": None,
     }
+    log(f"bench: dominant stage {dominant}: {rls[dominant]['achieved']:.1f} TFLOP/s = "
+        f"{100 * rls[dominant]['frac']:.1f}% of {rls[dominant]['peak']:.1f}")
     if not args.layer_only:
-        out["act_order"] = act_order_measure(g, torch, H, W, q, cfg, ws_u, ws_q)
+        out["act_order"] = act_order_measure(g, torch, leg["H"], W, leg["q"], cfg, leg["ws_u"], leg["ws_q"])
         ao = out["act_order"]
         log(f"bench: act-order path after H {ao['ms_after_hessian']:.3f} ms {ao['stages_ms']}; "
             f"loss {ao['loss_act_order']:.6g} (natural order {ao['loss_natural_order']:.6g})")
-        out["dequant_matvec"] = matvec_measure(g, torch, q, W, cfg)
+        out["dequant_matvec"] = matvec_measure(g, torch, leg["q"], W, cfg)
         log(f"bench: packed matrix-vector product {out['dequant_matvec']['us']:.2f} us "
             f"({out['dequant_matvec']['gbps']:.0f} GB/s); dense fp16 {out['dequant_matvec']['fp16_dense_us']:.2f} us")
-        if X.dtype == torch.float16:
-            out["pipeline"] = pipeline_measure(g, torch, X, W, cfg)
+        del leg, X, W
+        torch.cuda.empty_cache()
+        cfg2 = CONFIGS[SECOND_LAYER] if cfg.name != SECOND_LAYER else None
+        if cfg2 is not None:
+            X2 = upload_activations(cfg2, torch, dev)
+            W2 = torch.from_numpy(weights(cfg2)).to(dev)
+            leg2 = layer_leg(g, torch, cfg2, X2, W2, 10, 3)
+            rl2 = stage_rooflines(cfg2, leg2["stages"])
+            out["second_layer"] = {
+                "workload": cfg2.name, "ms_per_step": leg2["ms"], "median_step_ms": leg2["median_ms"],
+                "stages_ms": leg2["stages"], "cold_step_ms": leg2["cold"],
+                "weight_cols_per_s": cfg2.d_col / (leg2["ms"] * 1e-3), "stage_rooflines": rl2, "steps": 10,
+            }
+            del leg2
+        else:
+            X2, W2, cfg2 = None, None, cfg
+        if X2 is not None and X2.dtype == torch.float16:
+            out["pipeline"] = pipeline_measure(g, torch, X2, W2, cfg2)
             pl = out["pipeline"]
             log(f"bench: q/k/v sharing one Hessian {pl['qkv_shared_input_ms']['total']:.2f} ms "
                 f"{pl['qkv_shared_input_ms']}")
@@ -524,6 +613,7 @@ def main():
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(cfg)
+        log(f"bench: oracle {out['cpu_baseline']['sample']}")
     print(json.dumps(out), flush=True)
 
 
