@@ -12,7 +12,19 @@
  * Conventions shared by every entry point
  *   - Pointers named as device pointers refer to GPU memory the caller
  *     allocated (for instance with torch). The library never allocates,
- *     frees or retains caller memory; it keeps no state between calls.
+ *     frees or retains caller memory.
+ *   - Process-wide state (created on first use, kept until the process
+ *     ends, never freed): gptq_prepare_hinv keeps, per device, one
+ *     auxiliary stream (default priority) and a small set of events for its
+ *     look-ahead, and serializes its own enqueueing with a host mutex, so
+ *     concurrent factor calls on different streams share that auxiliary
+ *     stream and their device work overlaps less; while a caller captures a
+ *     factor call into a graph, no other thread may call gptq_prepare_hinv
+ *     on that device (the shared auxiliary stream is then part of the
+ *     capture). gptq_quantize_layer_noalloc uses one static scratch array
+ *     per device (see there). The packed product caches the occupancy per
+ *     kernel, taken on the first device it runs on. Nothing else is kept
+ *     between calls.
  *   - All matrices are row-major and contiguous unless a leading dimension
  *     is given.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
@@ -44,8 +56,15 @@ typedef enum {
   GPTQ_E_INVALID_ARG = 1, /* a size, pointer or parameter is out of range   */
   GPTQ_E_UNSUPPORTED = 2, /* valid for the method but not implemented here  */
   GPTQ_E_WORKSPACE = 3,   /* ws_bytes smaller than the required size         */
-  GPTQ_E_HIP = 4          /* a HIP launch or runtime call failed             */
+  GPTQ_E_HIP = 4,         /* a HIP launch or runtime call failed             */
+  GPTQ_E_TOO_LARGE = 5    /* beyond the static scratch of the allocation-free
+                             entry point                                     */
 } gptq_status;
+
+/* Largest layer gptq_quantize_layer_noalloc takes: d_row * d_col weights
+   and d_row rows (its static scratch holds an fp32 working copy of W). */
+#define GPTQ_NOALLOC_MAX_WEIGHTS (1 << 24)
+#define GPTQ_NOALLOC_MAX_ROWS 65536
 
 typedef enum { GPTQ_F16 = 0, GPTQ_F32 = 1 } gptq_dtype;
 
@@ -156,6 +175,32 @@ int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col,
                         int bits, int64_t group_size, int64_t block, int symmetric,
                         uint8_t* codes, float* scales, int32_t* zeros, uint32_t* packed,
                         double* loss, float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 3 without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Same operation, arguments, outputs and kernels as gptq_quantize_layer,
+ * minus ws/ws_bytes: the fp32 working copy of W and the loss partials live
+ * in one static device array of the library (64 MiB + 64 KiB), which each
+ * GPU the library runs on holds from the library's load until the process
+ * ends. The call allocates nothing (no hipMalloc, no allocating library
+ * routine); it takes the array's device address once per device with
+ * hipGetSymbolAddress. Nothing in the array needs clearing between calls.
+ *   Limits: d_row * d_col <= GPTQ_NOALLOC_MAX_WEIGHTS and d_row <=
+ *   GPTQ_NOALLOC_MAX_ROWS, else GPTQ_E_TOO_LARGE (checked before anything
+ *   is enqueued).
+ *   stream     must belong to the current device (else GPTQ_E_INVALID_ARG).
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (other streams, other threads) race and give undefined results;
+ * serialize them, or use gptq_quantize_layer with separate workspaces.
+ * Errors: as gptq_quantize_layer, plus GPTQ_E_TOO_LARGE.
+ * ---------------------------------------------------------------------- */
+int gptq_quantize_layer_noalloc(const void* W, int wdtype, int64_t d_row, int64_t d_col,
+                                const float* U, int bits, int64_t group_size, int64_t block,
+                                int symmetric, uint8_t* codes, float* scales, int32_t* zeros,
+                                uint32_t* packed, double* loss, float* row_loss, void* stream);
 
 /* ------------------------------------------------------------------------
  * Dequantize the packed layer (for running the quantized layer, e.g. to

@@ -20,7 +20,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgptq_mi355x.so")
 
-GPTQ_OK, GPTQ_E_INVALID_ARG, GPTQ_E_UNSUPPORTED, GPTQ_E_WORKSPACE, GPTQ_E_HIP = range(5)
+GPTQ_OK, GPTQ_E_INVALID_ARG, GPTQ_E_UNSUPPORTED, GPTQ_E_WORKSPACE, GPTQ_E_HIP, GPTQ_E_TOO_LARGE = range(6)
+GPTQ_NOALLOC_MAX_WEIGHTS, GPTQ_NOALLOC_MAX_ROWS = 1 << 24, 65536
 GPTQ_F16, GPTQ_F32 = 0, 1
 
 _lib: Optional[ctypes.CDLL] = None
@@ -38,6 +39,10 @@ _SIGNATURES = {
     "gptq_quantize_layer": (
         _c_int,
         [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr],
+    ),
+    "gptq_quantize_layer_noalloc": (
+        _c_int,
+        [_c_ptr, _c_int, _c_i64, _c_i64, _c_ptr, _c_int, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr],
     ),
     "gptq_pack_codes": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr]),
     "gptq_dequantize": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_int, _c_i64, _c_ptr]),
@@ -250,6 +255,51 @@ def gptq_quantize_layer(
             _ptr(W), _dtype_code(W), d_row, d_col, _ptr(U), bits, group_size, block, int(bool(symmetric)),
             _ptr(out.codes), _ptr(out.scales), _ptr(out.zeros), _ptr(out.packed), _ptr(out.loss),
             _ptr(out.row_loss), _ptr(ws), ws.numel(), _stream(),
+        ),
+    )
+    return out
+
+
+def _quantized_like(d_row: int, d_col: int, bits: int, group_size: int, want_row_loss: bool, dev) -> Quantized:
+    ng = n_groups(d_col, group_size) if group_size == -1 or group_size > 0 else 1
+    return Quantized(
+        codes=torch.empty((d_row, d_col), dtype=torch.uint8, device=dev),
+        scales=torch.empty((d_row, ng), dtype=torch.float32, device=dev),
+        zeros=torch.empty((d_row, ng), dtype=torch.int32, device=dev),
+        packed=torch.empty((d_row, words_per_row(d_col, bits)), dtype=torch.int32, device=dev),
+        loss=torch.empty((), dtype=torch.float64, device=dev),
+        row_loss=torch.empty((d_row,), dtype=torch.float32, device=dev) if want_row_loss else None,
+    )
+
+
+def gptq_quantize_layer_noalloc(
+    W: torch.Tensor,
+    U: torch.Tensor,
+    bits: int,
+    group_size: int,
+    block: int = 128,
+    out: Optional[Quantized] = None,
+    symmetric: bool = False,
+) -> Quantized:
+    """gptq_quantize_layer without a workspace: the library's static scratch
+    holds the working copy (at most GPTQ_NOALLOC_MAX_WEIGHTS weights and
+    GPTQ_NOALLOC_MAX_ROWS rows). Pass ``out`` to allocate nothing here either;
+    calls that overlap on one GPU race."""
+    _on_gpu("W", W)
+    _on_gpu("U", U)
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous 2-D tensor")
+    d_row, d_col = W.shape
+    if U.shape != (d_col, d_col) or U.dtype != torch.float32 or not U.is_contiguous():
+        raise ValueError("U must be a contiguous float32 [d_col, d_col] tensor")
+    if out is None:
+        out = _quantized_like(d_row, d_col, bits, group_size, True, W.device)
+    _check(
+        "gptq_quantize_layer_noalloc",
+        load().gptq_quantize_layer_noalloc(
+            _ptr(W), _dtype_code(W), d_row, d_col, _ptr(U), bits, group_size, block, int(bool(symmetric)),
+            _ptr(out.codes), _ptr(out.scales), _ptr(out.zeros), _ptr(out.packed), _ptr(out.loss),
+            _ptr(out.row_loss), _stream(),
         ),
     )
     return out

@@ -29,6 +29,7 @@
 // The first block reads the caller's W directly (no conversion pass).
 // Group statistics for a group that starts at column q are taken from the
 // current values when the sweep reaches q. The loss sum is kept in fp64.
+#include <mutex>
 #include <utility>
 
 #include "gptq_common.h"
@@ -506,10 +507,14 @@ extern "C" size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_co
   return carve_q(nullptr, d_row, d_col).bytes;
 }
 
-extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U, int bits,
-                                   int64_t group_size, int64_t block, int symmetric, uint8_t* codes, float* scales,
-                                   int32_t* zeros, uint32_t* packed, double* loss, float* row_loss, void* ws,
-                                   size_t ws_bytes, void* stream) {
+namespace gptq {
+namespace {
+
+// Argument checks shared by both sweep entry points (nothing is touched
+// before they pass).
+int check_quantize_args(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U, int bits,
+                        int64_t group_size, int64_t block, int symmetric, const uint8_t* codes, const float* scales,
+                        const int32_t* zeros, const uint32_t* packed, const double* loss) {
   if (d_row < 1 || d_col < 1 || d_row > (int64_t(1) << 30) || d_col > (1 << 20)) return GPTQ_E_INVALID_ARG;
   if (d_row * d_col > (int64_t(1) << 40)) return GPTQ_E_INVALID_ARG;
   if (!W || !U || !codes || !scales || !zeros || !packed || !loss) return GPTQ_E_INVALID_ARG;
@@ -521,9 +526,14 @@ extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int
   }
   if (block != QB) return GPTQ_E_UNSUPPORTED;
   if (group_size != -1 && group_size % 16 != 0) return GPTQ_E_UNSUPPORTED;
-  const QuantWs w = carve_q(ws, d_row, d_col);
-  if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_E_WORKSPACE;
-  hipStream_t s = as_stream(stream);
+  return GPTQ_OK;
+}
+
+// The sweep and the loss sum on stream s, with the working copy and loss
+// partials at w (arguments already checked).
+int launch_quantize(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U, int bits,
+                    int64_t group_size, int symmetric, uint8_t* codes, float* scales, int32_t* zeros,
+                    uint32_t* packed, double* loss, float* row_loss, const QuantWs& w, hipStream_t s) {
   const int ngroups = group_size == -1 ? 1 : int((d_col + group_size - 1) / group_size);
   const int nwords = int((d_col * bits + 31) / 32);
   const int esz = wdtype == GPTQ_F16 ? 2 : 4;
@@ -560,6 +570,79 @@ extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int
   return launch_status();
 }
 
+// Scratch of the allocation-free sweep entry point: the fp32 working copy
+// of W (at most GPTQ_NOALLOC_MAX_WEIGHTS elements) followed by the
+// per-workgroup loss partials (at most GPTQ_NOALLOC_MAX_ROWS / 16 doubles).
+// Each GPU the library runs on holds its own copy until the process ends.
+// In host code `scratch` names a host-side stand-in, never a device
+// address: its device address comes from hipGetSymbolAddress, per device.
+constexpr size_t NOALLOC_WF_BYTES = size_t(GPTQ_NOALLOC_MAX_WEIGHTS) * sizeof(float);
+constexpr size_t NOALLOC_BYTES = NOALLOC_WF_BYTES + 65536;
+static_assert(NOALLOC_WF_BYTES % 256 == 0, "loss partials must start 256-byte aligned");
+static_assert((GPTQ_NOALLOC_MAX_ROWS / QR) * sizeof(double) <= 65536, "loss partials must fit");
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of `scratch` on the current device, taken once per
+// device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return GPTQ_E_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return GPTQ_E_HIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return GPTQ_OK;
+}
+
+}  // namespace
+}  // namespace gptq
+
+extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U, int bits,
+                                   int64_t group_size, int64_t block, int symmetric, uint8_t* codes, float* scales,
+                                   int32_t* zeros, uint32_t* packed, double* loss, float* row_loss, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  const int st = check_quantize_args(W, wdtype, d_row, d_col, U, bits, group_size, block, symmetric, codes, scales,
+                                     zeros, packed, loss);
+  if (st != GPTQ_OK) return st;
+  const QuantWs w = carve_q(ws, d_row, d_col);
+  if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_E_WORKSPACE;
+  return launch_quantize(W, wdtype, d_row, d_col, U, bits, group_size, symmetric, codes, scales, zeros, packed, loss,
+                         row_loss, w, as_stream(stream));
+}
+
+extern "C" int gptq_quantize_layer_noalloc(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U,
+                                           int bits, int64_t group_size, int64_t block, int symmetric,
+                                           uint8_t* codes, float* scales, int32_t* zeros, uint32_t* packed,
+                                           double* loss, float* row_loss, void* stream) {
+  const int st = check_quantize_args(W, wdtype, d_row, d_col, U, bits, group_size, block, symmetric, codes, scales,
+                                     zeros, packed, loss);
+  if (st != GPTQ_OK) return st;
+  if (d_row > GPTQ_NOALLOC_MAX_ROWS || d_row * d_col > GPTQ_NOALLOC_MAX_WEIGHTS) return GPTQ_E_TOO_LARGE;
+  hipStream_t s = as_stream(stream);
+  if (s != nullptr) {  // the scratch used is the current device's: the stream must belong to it
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess) return GPTQ_E_HIP;
+    if (cur != sdev) return GPTQ_E_INVALID_ARG;
+  }
+  void* base = nullptr;
+  const int sa = scratch_address(&base);
+  if (sa != GPTQ_OK) return sa;
+  const QuantWs w = carve_q(base, d_row, d_col);
+  if (w.bytes > NOALLOC_BYTES) return GPTQ_E_TOO_LARGE;
+  // Nothing in the scratch must start at zero: every working-copy element
+  // the sweep reads was written earlier in the same launch, and every loss
+  // partial is written before loss_final reads it.
+  return launch_quantize(W, wdtype, d_row, d_col, U, bits, group_size, symmetric, codes, scales, zeros, packed, loss,
+                         row_loss, w, s);
+}
+
 extern "C" int gptq_pack_codes(const uint8_t* codes, int64_t d_row, int64_t d_col, int bits, uint32_t* packed,
                                void* stream) {
   if (d_row < 1 || d_col < 1 || d_col > (1 << 24) || !codes || !packed || !bits_ok(bits)) return GPTQ_E_INVALID_ARG;
@@ -579,6 +662,7 @@ extern "C" const char* gptq_status_string(int status) {
     case GPTQ_E_UNSUPPORTED: return "unsupported parameter";
     case GPTQ_E_WORKSPACE: return "workspace too small";
     case GPTQ_E_HIP: return "HIP launch or runtime error";
+    case GPTQ_E_TOO_LARGE: return "layer larger than the allocation-free entry point's static scratch";
     default: return "unknown status";
   }
 }
