@@ -413,14 +413,17 @@ def test_quantize_is_deterministic(gpu):
 
 
 # -------------------------------------------------------------------- pack
-@pytest.mark.parametrize("wdt,bits,group", [(np.float16, 3, 128), (np.float32, 4, -1)])
+@pytest.mark.parametrize("wdt,bits,group", [(np.float16, 3, 128), (np.float32, 4, -1), (np.float16, 4, 256),
+                                            (np.float16, 3, 512), (np.float16, 4, 384)])
 def test_tall_layer_row_groups_are_bit_identical(gpu, wdt, bits, group):
     """Tile-aligned layers with at least 16384 rows (a multiple of 32) and
-    12288 columns take 32 rows per workgroup, others 16. A row's arithmetic
-    is the same either way, so the 16384-row layer and the same layer one
-    16-row group shorter agree bit for bit on the rows both have; the tall
-    one also matches the oracle on sampled rows. U is any upper-triangular
-    factor with a positive diagonal (both sides take it as given)."""
+    12288 columns take 32 rows per workgroup, others 16. A row's MFMA
+    sequence is the same either way, so the 16384-row layer and the same
+    layer one 16-row group shorter agree bit for bit on the rows both have;
+    the tall one also matches the oracle on sampled rows. Groups wider than
+    a block (256, 384, 512) read columns past the block for their
+    statistics. U is any upper-triangular factor with a positive diagonal
+    (both sides take it as given)."""
     d_row, d_col = 16384, 12288
     r = np.random.default_rng(98)
     U = (np.triu(r.standard_normal((d_col, d_col), dtype=np.float32)) * 1e-3 + np.eye(d_col, dtype=np.float32))

@@ -128,23 +128,25 @@ def test_identity_hessian_reduces_to_rtn(bits, group):
     assert out["loss"] == pytest.approx(0.5 * (1 + lam) * np.sum((W - what) ** 2), rel=1e-12)
 
 
-def _demo_nearest_quant(w, bits):
-    # Round-to-nearest of the aiqz.cc demo (section Python 演示), written out
-    # here on its own: scale = max|w| / qmax, clip(round(w / scale), -qmax,
-    # qmax) * scale, qmax = 2^(b-1) - 1.
-    qmax = 2 ** (bits - 1) - 1
-    scale = np.abs(w).max() / qmax
-    return np.clip(np.round(w / scale), -qmax, qmax) * scale
+def _symmetric_grid_rounding(w, bits):
+    # The symmetric quantizer as defined in the astro-blog survey, section 1.2
+    # (zero point 0, signed codes on [-2^(b-1), 2^(b-1) - 1]), with the scale
+    # that maps the largest magnitude to the largest positive code:
+    # s = max|w| / (2^(b-1) - 1); code = clamp(rint(w / s)); value s * code.
+    top = 2 ** (bits - 1) - 1
+    s = np.abs(w).max() / top
+    code = np.clip(np.rint(w / s), -top - 1, top)
+    return s * code
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 @pytest.mark.parametrize("group", [-1, 16])
-def test_symmetric_identity_hessian_is_demo_rounding(bits, group):
+def test_symmetric_identity_hessian_is_plain_rounding(bits, group):
     W = 0.02 * rng(40 + bits).standard_normal((6, 32))
     U, _ = O.prepare_hinv(np.eye(32), 0.0)  # U = I: nothing is compensated
     out = O.quantize_layer(W, U, bits, group, block=8, symmetric=True)
     g = 32 if group == -1 else group
-    ref = np.hstack([np.vstack([_demo_nearest_quant(r, bits) for r in W[:, k : k + g]]) for k in range(0, 32, g)])
+    ref = np.hstack([np.vstack([_symmetric_grid_rounding(r, bits) for r in W[:, k : k + g]]) for k in range(0, 32, g)])
     assert np.array_equal(out["Wq"], ref)
     assert np.all(out["zeros"] == 2 ** (bits - 1))
 
