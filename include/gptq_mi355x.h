@@ -150,7 +150,13 @@ int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* l
  *   bits       2, 3, 4 or 8.
  *   group_size -1, or a multiple of 16 with block % group_size == 0 or
  *              group_size % block == 0.
- *   block      128 (the lazy-batch width; other widths -> UNSUPPORTED).
+ *   block      the lazy-batch width B (xuzou.cn, section 方法适配: updates
+ *              of later columns wait until a block of B columns is done):
+ *              a power of two up to 128, or a multiple of 128 up to 1024;
+ *              other widths -> UNSUPPORTED. Lazy batches are exact, and the
+ *              kernels apply every element's fp32 updates in the same order
+ *              for every width, so all widths give the same outputs to the
+ *              bit; 128 is the fastest (it is the kernels' own block).
  *   symmetric  0: the min-max grid above. 1: the symmetric grid (astro-blog
  *              survey, section 1.2: z = 0, signed values clamped to
  *              [-2^(bits-1), 2^(bits-1) - 1]; aiqz.cc demo scale): s =
@@ -166,8 +172,9 @@ int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* l
  *              zero padded.
  *   loss       device fp64 scalar (sum over rows and columns).
  *   row_loss   device fp32 d_row, may be NULL.
- * Errors: sizes < 1, NULL outputs (row_loss excepted), bad bits or group
- * -> GPTQ_E_INVALID_ARG; block != 128 -> GPTQ_E_UNSUPPORTED.
+ * Errors: sizes < 1, NULL outputs (row_loss excepted), bad bits or group,
+ * block < 1 -> GPTQ_E_INVALID_ARG; a block width outside the set above, or
+ * a group that is not a multiple of 16 -> GPTQ_E_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
 size_t gptq_quantize_layer_workspace_size(int64_t d_row, int64_t d_col, int bits,
                                           int64_t group_size, int64_t block);

@@ -51,6 +51,8 @@ constexpr int RG2_MIN_COLS = 12288;
 // Whole-tile layers of at most this many 16-row workgroups (one per CU)
 // take 8 waves per workgroup.
 constexpr int XW2_MAX_WG = 256;
+// Largest lazy-batch width (a multiple of QB) the sweep takes.
+constexpr int LZ_MAX_B = 1024;
 
 template <int Q, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -142,8 +144,14 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
         v[g][r] = first ? load4(W + off) : load4(Wf + off);
       }
   };
-  constexpr int RING = RG == 1 ? 8 : 4;  // U k-steps in flight (RG = 2: within 256 registers)
+  // U k-steps in flight. RG = 2 reads its A operands from LDS one k-step
+  // ahead instead of keeping all 64 of them in registers, which leaves room
+  // for a deeper ring.
+  constexpr int RING = RG == 1 ? 8 : sizeof(WT) == 2 ? 16 : 8;
   constexpr int KS4 = QB / 4;             // k-steps per chunk
+  // Step t of a chunk uses slot t % RING, and the last RING steps prefetch
+  // the next chunk's first steps into their own slots: RING must divide KS4.
+  static_assert(KS4 % RING == 0, "the ring's slots must line up across chunks");
   floatx4 ring[RING];
   floatx4 wn[RG][4];
   if (nch > 0) {
@@ -161,6 +169,11 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
         for (int t = 0; t < 4; ++t) acc[g][t][r] = wn[g][r][t];
     const bool more = ch + 1 < nch;
     if (more) ldw(ch + 1, wn);
+    float an[RG];  // RG = 2: the next k-step's A operands
+    if constexpr (RG > 1) {
+#pragma unroll
+      for (int g = 0; g < RG; ++g) an[g] = -Es[16 * g + li][lk];
+    }
 #pragma unroll
     for (int t = 0; t < KS4; ++t) {
       const floatx4 b = ring[t % RING];
@@ -168,11 +181,23 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
         ring[t % RING] = ldb(ch, t + RING);
       else if (more)
         ring[t % RING] = ldb(ch + 1, t + RING - KS4);
+      if constexpr (RG == 1) {
+        const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
 #pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        const float at = -Es[16 * g + li][4 * t + lk];  // A operand: row 16 g + li, k = 4t + lk
+        for (int v = 0; v < 4; ++v) acc[0][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[0][v], 0, 0, 0);
+      } else {
+        float a[RG];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[g][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[g][v], 0, 0, 0);
+        for (int g = 0; g < RG; ++g) a[g] = an[g];
+        if (t + 1 < KS4) {
+#pragma unroll
+          for (int g = 0; g < RG; ++g) an[g] = -Es[16 * g + li][4 * (t + 1) + lk];
+        }
+        asm volatile("" ::: "memory");  // each step's reads stay in their step (no hoisting)
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[g][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g], b[v], acc[g][v], 0, 0, 0);
       }
     }
 #pragma unroll
@@ -189,16 +214,30 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
 // many waves in the deferred update: with XW = 2 the waves beyond the row
 // groups' 4 RG take part only in that update (and in the workgroup's
 // barriers). RG > 1 and XW > 1 only for the whole-tile form.
-template <typename WT, bool WHOLE, int RG, int XW>
-__global__ void __launch_bounds__(QT * RG * XW, RG * XW == 1 ? 2 : 1)
+//
+// LZ = 2 selects a lazy-batch width B (`lazyb`) that is a multiple of QB, up
+// to LZ_MAX_B, in the checked form: inside a B-column block each 128-column
+// block's errors reach only the rest of the B-block; at the B-block's end the
+// later columns receive all of its errors in one pass (the B-block's errors
+// are kept in LDS). Widths that divide QB nest inside the 128-column block,
+// whose in-block updates are eager in registers: a column past a B-column
+// sub-block then receives the sub-block's errors one by one in column order,
+// exactly as deferring them to the sub-block's end would apply them, so
+// those widths run the LZ = 0 form. Each element sees the same fp32
+// operations in the same order for every B, so every B gives the same
+// results to the bit, as the method's exact lazy batches promise.
+template <typename WT, bool WHOLE, int RG, int XW, int LZ = 0>
+__global__ void __launch_bounds__(QT * RG * XW, RG * XW == 1 && LZ == 0 ? 2 : 1)
 gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __restrict__ U, int d_row, int d_col,
            int bits, int sym, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
            int32_t* __restrict__ zeros, uint32_t* __restrict__ packed, int nwords, float* __restrict__ row_loss,
-           double* __restrict__ wg_loss) {
+           double* __restrict__ wg_loss, int lazyb) {
   static_assert(WHOLE || (RG == 1 && XW == 1), "the checked form takes one row group of 4 waves");
+  static_assert(LZ == 0 || !WHOLE, "other lazy-batch widths take the checked form");
   constexpr int NT = QT * RG * XW, NR = QR * RG;  // threads and rows per workgroup
+  constexpr int EW = LZ == 2 ? LZ_MAX_B : QB;     // error columns kept in LDS
   __shared__ __attribute__((aligned(16))) float Ud[QB][QB];
-  __shared__ float Es[NR][QB + 4];
+  __shared__ float Es[NR][EW + 4];
   __shared__ uint8_t Cs[NR][QB];
   __shared__ double Lsum[NR];
 
@@ -236,6 +275,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
   for (int i1 = 0; i1 < d_col; i1 += QB) {
     const int nvalid = d_col - i1 < QB ? d_col - i1 : QB;
     const bool first = (i1 == 0);
+    const int kk0 = LZ == 2 ? i1 % lazyb : 0;  // this block's first error column in Es
 
     // 1. U block (upper part; padded columns act as identity rows) and W block.
     if (vec4 && nvalid == QB) {
@@ -341,7 +381,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       // Every lane of the row holds the same code and error: all 16 store
       // the same value to the row's LDS slot, so no owner test is needed.
       Cs[rloc][q] = uint8_t(c);
-      Es[rloc][q] = e;
+      Es[rloc][kk0 + q] = e;
       if constexpr (q + 1 < QB) {
 #pragma unroll
         for (int mm = (q + 1) / 16; mm < QM; ++mm) uc[mm] = un[mm];
@@ -368,6 +408,86 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
     const int i2 = i1 + QB;
     if constexpr (WHOLE) {
       if (i2 < d_col) trailing_update_whole<WT, RG, XW>(W, Wf, U, Es, d_col, row0, i1, first);
+    } else if (LZ == 2) {
+      // Inside a B-block, this block's errors go to the rest of the B-block;
+      // at its end, all of the B-block's errors go to the later columns (a
+      // B-block followed by columns is always complete). At most one of the
+      // two runs per block. Columns are bounded by n_hi, not d_col: those
+      // past the B-block must not receive this block's errors yet.
+      const int o1 = i1 - kk0;
+      const int o2 = o1 + lazyb < d_col ? o1 + lazyb : d_col;
+      const bool inner = i2 < o2;
+      if (inner || o2 < d_col) {
+        const int n_lo = inner ? i2 : o2, n_hi = inner ? o2 : d_col;
+        const int k0 = inner ? i1 : o1;          // U row of the first error
+        const int ec0 = inner ? kk0 : 0;         // Es column of the first error
+        const int nsub = inner ? 1 : lazyb / QB;  // blocks of errors applied
+        const bool fst = inner ? first : o1 == 0;
+        const int li = lane & 15, lk = lane >> 4;
+        for (int n0 = n_lo + 64 * wave; n0 < n_hi; n0 += 256) {
+          const int col = n0 + 4 * li;
+          const bool full = vec4 && (n0 + 64 <= n_hi);
+          floatx4 acc[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rr = row0 + 4 * lk + r;
+            floatx4 v = {0.f, 0.f, 0.f, 0.f};
+            if (rr < d_row) {
+              const size_t off = size_t(rr) * d_col + col;
+              if (full) {
+                v = fst ? load4(W + off) : load4(Wf + off);
+              } else {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  if (col + t < n_hi) v[t] = fst ? to_f(W[off + t]) : Wf[off + t];
+              }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t][r] = v[t];
+          }
+          const uint32_t ustep = uint32_t(4 * d_col);
+          for (int sb = 0; sb < nsub; ++sb) {
+            const float* ub = U + size_t(k0 + QB * sb + lk) * d_col + col;
+            auto ldb = [&](int t) -> floatx4 {
+              const float* p = ub + uint32_t(t) * ustep;
+              floatx4 b = {0.f, 0.f, 0.f, 0.f};
+              if (full) {
+                b = load4(p);
+              } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                  if (col + u < n_hi) b[u] = p[u];
+              }
+              return b;
+            };
+            constexpr int RING = 8;
+            floatx4 ring[RING];
+#pragma unroll
+            for (int t = 0; t < RING; ++t) ring[t] = ldb(t);
+#pragma unroll
+            for (int t = 0; t < QB / 4; ++t) {
+              const float at = -Es[li][ec0 + QB * sb + 4 * t + lk];  // A operand: row li, k = 128 sb + 4t + lk
+              const floatx4 b = ring[t % RING];
+              if (t + RING < QB / 4) ring[t % RING] = ldb(t + RING);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) acc[v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[v], 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int rr = row0 + 4 * lk + r;
+            if (rr >= d_row) continue;
+            const size_t off = size_t(rr) * d_col + col;
+            if (full) {
+              *reinterpret_cast<float4*>(Wf + off) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t)
+                if (col + t < n_hi) Wf[off + t] = acc[t][r];
+            }
+          }
+        }
+      }
     } else if (i2 < d_col) {
       const int li = lane & 15, lk = lane >> 4;
       for (int n0 = i2 + 64 * wave; n0 < d_col; n0 += 256) {
@@ -524,7 +644,9 @@ int check_quantize_args(const void* W, int wdtype, int64_t d_row, int64_t d_col,
   if (group_size != -1) {
     if (group_size < 1 || (block % group_size != 0 && group_size % block != 0)) return GPTQ_E_INVALID_ARG;
   }
-  if (block != QB) return GPTQ_E_UNSUPPORTED;
+  // lazy-batch widths: a power of two up to QB, or a multiple of QB up to LZ_MAX_B
+  if (!(block <= QB && (block & (block - 1)) == 0) && !(block % QB == 0 && block <= LZ_MAX_B))
+    return GPTQ_E_UNSUPPORTED;
   if (group_size != -1 && group_size % 16 != 0) return GPTQ_E_UNSUPPORTED;
   return GPTQ_OK;
 }
@@ -532,7 +654,7 @@ int check_quantize_args(const void* W, int wdtype, int64_t d_row, int64_t d_col,
 // The sweep and the loss sum on stream s, with the working copy and loss
 // partials at w (arguments already checked).
 int launch_quantize(const void* W, int wdtype, int64_t d_row, int64_t d_col, const float* U, int bits,
-                    int64_t group_size, int symmetric, uint8_t* codes, float* scales, int32_t* zeros,
+                    int64_t group_size, int64_t block, int symmetric, uint8_t* codes, float* scales, int32_t* zeros,
                     uint32_t* packed, double* loss, float* row_loss, const QuantWs& w, hipStream_t s) {
   const int ngroups = group_size == -1 ? 1 : int((d_col + group_size - 1) / group_size);
   const int nwords = int((d_col * bits + 31) / 32);
@@ -542,7 +664,10 @@ int launch_quantize(const void* W, int wdtype, int64_t d_row, int64_t d_col, con
   // Whole-tile layers (every chunk of the deferred update complete, every
   // workgroup's rows present) take the branch-free update; tall and wide ones
   // take 32 rows per workgroup, halving the U rows each row's update streams.
-  const bool whole = vec4 && d_col % 64 == 0 && d_row % QR == 0;
+  // Lazy-batch widths above the block take the checked form with two-level
+  // deferral; those that divide the block nest inside it (see gptq_sweep).
+  const int lz = block > QB ? 2 : 0;
+  const bool whole = lz == 0 && vec4 && d_col % 64 == 0 && d_row % QR == 0;
   const int rg = (whole && d_row % (2 * QR) == 0 && d_row >= RG2_MIN_ROWS && d_col >= RG2_MIN_COLS) ? 2 : 1;
   const unsigned nwg = unsigned((d_row + rg * QR - 1) / (rg * QR));
   // Layers small enough that every CU holds at most one 16-row workgroup
@@ -552,18 +677,20 @@ int launch_quantize(const void* W, int wdtype, int64_t d_row, int64_t d_col, con
     auto k = rg == 2 ? gptq_sweep<__half, true, 2, 1>
              : xw == 2 ? gptq_sweep<__half, true, 1, 2>
              : whole ? gptq_sweep<__half, true, 1, 1>
+             : lz == 2 ? gptq_sweep<__half, false, 1, 1, 2>
                      : gptq_sweep<__half, false, 1, 1>;
     hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * xw * QT), 0, s, static_cast<const __half*>(W), w.Wf, U, int(d_row),
                        int(d_col), bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords,
-                       row_loss, w.wg_loss);
+                       row_loss, w.wg_loss, int(block));
   } else {
     auto k = rg == 2 ? gptq_sweep<float, true, 2, 1>
              : xw == 2 ? gptq_sweep<float, true, 1, 2>
              : whole ? gptq_sweep<float, true, 1, 1>
+             : lz == 2 ? gptq_sweep<float, false, 1, 1, 2>
                      : gptq_sweep<float, false, 1, 1>;
     hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * xw * QT), 0, s, static_cast<const float*>(W), w.Wf, U, int(d_row),
                        int(d_col), bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords,
-                       row_loss, w.wg_loss);
+                       row_loss, w.wg_loss, int(block));
   }
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   hipLaunchKernelGGL(loss_final, dim3(1), dim3(256), 0, s, w.wg_loss, int(nwg), loss);
@@ -613,7 +740,7 @@ extern "C" int gptq_quantize_layer(const void* W, int wdtype, int64_t d_row, int
   if (st != GPTQ_OK) return st;
   const QuantWs w = carve_q(ws, d_row, d_col);
   if (ws == nullptr || ws_bytes < w.bytes) return GPTQ_E_WORKSPACE;
-  return launch_quantize(W, wdtype, d_row, d_col, U, bits, group_size, symmetric, codes, scales, zeros, packed, loss,
+  return launch_quantize(W, wdtype, d_row, d_col, U, bits, group_size, block, symmetric, codes, scales, zeros, packed, loss,
                          row_loss, w, as_stream(stream));
 }
 
@@ -639,7 +766,7 @@ extern "C" int gptq_quantize_layer_noalloc(const void* W, int wdtype, int64_t d_
   // Nothing in the scratch must start at zero: every working-copy element
   // the sweep reads was written earlier in the same launch, and every loss
   // partial is written before loss_final reads it.
-  return launch_quantize(W, wdtype, d_row, d_col, U, bits, group_size, symmetric, codes, scales, zeros, packed, loss,
+  return launch_quantize(W, wdtype, d_row, d_col, U, bits, group_size, block, symmetric, codes, scales, zeros, packed, loss,
                          row_loss, w, s);
 }
 

@@ -307,6 +307,43 @@ def test_quantize_layer_parity(gpu, d_row, d_col, bits, group, wdt):
     assert float(q.loss.item()) == pytest.approx(float(np.sum(q.row_loss.cpu().numpy().astype(np.float64))), rel=1e-6)
 
 
+LAZY_SHAPES = [
+    (40, 1300, 4, -1, np.float32),  # ragged: 10 full blocks and a 20-column tail
+    (64, 2048, 3, 128, np.float16),  # whole tiles
+    (33, 1100, 4, 16, np.float16),
+]
+
+
+@pytest.mark.parametrize("d_row,d_col,bits,group,wdt", LAZY_SHAPES)
+def test_lazy_batch_widths(gpu, d_row, d_col, bits, group, wdt):
+    """Lazy batches are exact (the deferred update applies the same rank-1
+    updates later), so every width gives the same layer: on the GPU each
+    element sees the same fp32 operations in the same order for every width
+    (widths above the block defer in two levels, widths that divide it nest
+    inside it), so all widths agree to the bit with B = 128; each also passes
+    the oracle's own sweep at that width."""
+    say("lazy widths", d_row, d_col, bits, group, wdt.__name__)
+    U = oracle_u(d_col, d_col + 3 * bits)
+    W = (0.02 * np.random.default_rng(d_row * d_col).standard_normal((d_row, d_col))).astype(wdt)
+    Wd, Ud = gpu_tensor(W), gpu_tensor(U)
+    base = gpu.gptq_quantize_layer(Wd, Ud, bits, group, 128)
+    widths = [1, 2, 16, 64, 256, 512, 1024]
+    outs = {}
+    for B in widths:
+        if group != -1 and B % group and group % B:
+            continue  # blocks and groups must nest
+        outs[B] = gpu.gptq_quantize_layer(Wd, Ud, bits, group, B)
+    torch.cuda.synchronize()
+    for B, q in outs.items():
+        for name in ("codes", "scales", "zeros", "packed", "row_loss", "loss"):
+            assert torch.equal(getattr(q, name).reshape(-1).view(torch.uint8),
+                               getattr(base, name).reshape(-1).view(torch.uint8)), (B, name)
+    for B in (1, 256, 1024):
+        if B in outs:
+            ref = O.quantize_layer(W, U, bits, group, B, decide=np.float32)
+            check_quant(outs[B], ref, bits, rerun_for(W, U, bits, group, B), label=f"block {B}")
+
+
 @pytest.mark.parametrize("bits,group", [(4, -1), (3, 128), (2, 32), (8, 16)])
 def test_identity_hessian_is_rtn_bit_exact(gpu, bits, group):
     d_col = 384
@@ -478,7 +515,7 @@ def test_abi_rejects_bad_arguments(gpu):
         gpu.gptq_quantize_layer(W, U, 4, 48)  # neither divides the other
     assert e.value.status == gpu.GPTQ_E_INVALID_ARG
     with pytest.raises(gpu.GptqError) as e:
-        gpu.gptq_quantize_layer(W, U, 4, -1, block=64)
+        gpu.gptq_quantize_layer(W, U, 4, -1, block=96)  # neither a power of two below 128 nor a multiple of 128
     assert e.value.status == gpu.GPTQ_E_UNSUPPORTED
     with pytest.raises(gpu.GptqError) as e:
         gpu.gptq_prepare_hinv(U, damp=-1.0)
