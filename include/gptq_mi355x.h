@@ -229,6 +229,35 @@ int gptq_dequantize(const uint32_t* packed, const float* scales, const int32_t* 
                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * Running the quantized layer on token batches (the calibration pipeline's
+ * propagation to the next layer).
+ *
+ * Defines: xuzou.cn reading card of the GPTQ paper, section 计算设置 (each
+ * quantized block is run on the calibration tokens to give the next block's
+ * inputs) and section 方法适配, last paragraph (the quantized matrix is used
+ * with dequantization on the fly); What = s (code - z) per group (astro-blog
+ * survey, section 1.2), held as fp16 to run. For t < n_tokens, r < d_out:
+ *   Y[t][r] = act(sum_c X[t][c] * W16[r][c]),
+ *   W16[r][c] = fp16(fp32(scales[r][g(c)] * (code[r][c] - zeros[r][g(c)]))),
+ * act = ReLU when relu = 1 (identity when 0), Y rounded to fp16 (nearest
+ * even). The products of fp16 values are exact in fp32 and the sums are
+ * fp32, on the fp16 MFMA (the weights are dequantized inside the kernel,
+ * never written out).
+ *   packed, scales, zeros   as for gptq_quantize_layer (d_out rows, d_in
+ *              columns; bits 2, 3, 4 or 8).
+ *   X          device fp16, n_tokens rows of d_in values, row stride ldx.
+ *   Y          device fp16, n_tokens x d_out, row stride ldy >= d_out.
+ * Runs on `stream`; nothing is allocated; n_tokens = 0 does nothing.
+ * Errors: sizes < 1, NULL pointers, ldx < d_in, ldy < d_out, bad bits,
+ * group_size 0 or < -1, relu not 0 or 1 -> GPTQ_E_INVALID_ARG; d_in not a
+ * multiple of 32, group_size not -1 or a multiple of 64, X not 16-byte
+ * aligned or ldx not a multiple of 8 -> GPTQ_E_UNSUPPORTED.
+ * ---------------------------------------------------------------------- */
+int gptq_dequant_gemm(const uint32_t* packed, const float* scales, const int32_t* zeros, int64_t d_out,
+                      int64_t d_in, int bits, int64_t group_size, const void* X, int64_t n_tokens,
+                      int64_t ldx, void* Y, int64_t ldy, int relu, void* stream);
+
+/* ------------------------------------------------------------------------
  * Column order: act-order permutation.
  *
  * Defines: mcipr.com "一文读懂GPTQ", section 四 (the desc_act flag of the

@@ -557,6 +557,19 @@ def model_weight_f16(codes, scales, zeros, group_size: int) -> np.ndarray:
     return (s32 * k32).astype(np.float16)
 
 
+def run_quantized_layer(X, packed, scales, zeros, d_in: int, bits: int, group_size: int, relu: bool = False):
+    """The quantized layer run on tokens X [n, d_in] (xuzou.cn reading card,
+    section 计算设置: the quantized block produces the next block's
+    inputs): Y = act(X What^T) with What the fp16 model weight of
+    ``model_weight_f16`` decoded from the packed words, the product exact
+    (float64), act = ReLU if ``relu``, and Y rounded to fp16."""
+    Wh = model_weight_f16(unpack(packed, d_in, bits), scales, zeros, group_size).astype(F64)
+    Y = np.asarray(X, dtype=F64) @ Wh.T
+    if relu:
+        Y = np.maximum(Y, 0.0)
+    return Y.astype(np.float16)
+
+
 def quantize_mlp_block(X0, W_up, W_down, bits: int, group_size: int, block: int = 128, damp: float = 0.01,
                        decide=F64):
     """One MLP block quantized layer by layer (xuzou.cn reading card,

@@ -51,6 +51,10 @@ _SIGNATURES = {
         _c_int,
         [_c_ptr, _c_int, _c_i64, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr],
     ),
+    "gptq_dequant_gemm": (
+        _c_int,
+        [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_int, _c_ptr],
+    ),
     "gptq_dequant_matvec": (
         _c_int,
         [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr],
@@ -435,3 +439,28 @@ def gptq_dequant_matvec(
         ),
     )
     return y.squeeze(0) if x.dim() == 1 else y
+
+
+def gptq_dequant_gemm(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, d_in: int, bits: int,
+                      group_size: int, X: torch.Tensor, relu: bool = False,
+                      Y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = act(X What^T) (fp16) for the packed layer [d_out rows] and fp16
+    tokens X [n, d_in]; act is ReLU with ``relu``."""
+    for n, t in (("packed", packed), ("scales", scales), ("zeros", zeros), ("X", X)):
+        _on_gpu(n, t)
+    if X.dtype != torch.float16 or X.dim() != 2 or X.stride(1) != 1 or X.shape[1] != d_in:
+        raise ValueError("X must be a 2-D fp16 tensor [n, d_in] with unit column stride")
+    d_out = packed.shape[0]
+    n = X.shape[0]
+    if Y is None:
+        Y = torch.empty((n, d_out), dtype=torch.float16, device=X.device)
+    if Y.dtype != torch.float16 or Y.shape != (n, d_out) or Y.stride(1) != 1:
+        raise ValueError("Y must be fp16 [n, d_out] with unit column stride")
+    ldx = X.stride(0) if n > 1 else d_in
+    ldy = Y.stride(0) if n > 1 else d_out
+    _check(
+        "gptq_dequant_gemm",
+        load().gptq_dequant_gemm(_ptr(packed), _ptr(scales), _ptr(zeros), d_out, d_in, bits, group_size, _ptr(X), n,
+                                 ldx, _ptr(Y), ldy, int(bool(relu)), _stream()),
+    )
+    return Y

@@ -22,8 +22,9 @@
 //    split writes its partial tile to the workspace; a second kernel sums the
 //    splits in a fixed order in fp64, scales by 2, mirrors the upper tiles
 //    into both triangles and applies accumulate. No atomics: deterministic.
-//  * fp32 inputs take a plain VALU tile kernel (64x64 tiles, same partials
-//    and reduction).
+//  * fp32 inputs take the fp32 MFMA (v_mfma_f32_32x32x2f32) on 64x64 tiles
+//    with the same token splits, partials and reduction; X is not rounded
+//    to fp16.
 #include "gptq_common.h"
 
 namespace gptq {
@@ -32,7 +33,7 @@ namespace {
 constexpr int SY_T = 256;         // tile edge (fp16 MFMA kernel)
 constexpr int SY_BK = 32;         // tokens per LDS stage
 constexpr int SY_THREADS = 256;
-constexpr int SYF_T = 64;         // tile edge (fp32 VALU kernel)
+constexpr int SYF_T = 64;         // tile edge (fp32 MFMA kernel)
 constexpr int SYF_BK = 16;
 
 // Upper-triangle tile index -> (bi, bj), row-major over bi <= bj.
@@ -424,12 +425,18 @@ syrk_f16_lds(const __half* __restrict__ X, int64_t n_main, int64_t ldx, int nb, 
       }
 }
 
-// fp32 inputs: VALU 64x64 tiles, 256 threads each holding a 4x4 block.
+// fp32 inputs: the same upper 64x64 tiles and token splits, on the fp32
+// MFMA. Four waves (2x2) each own a 32x32 block: one v_mfma_f32_32x32x2f32
+// per 2 tokens, whose A operand (lane l: channel I0 + 32 wi + l % 32, token
+// l / 32) and B operand (channel J0 + 32 wj + l % 32, same token) are
+// consecutive floats of one token row of the token-major LDS panels, so the
+// 64 lanes read without bank conflicts. The products and sums are fp32, as
+// the inputs are (no rounding of X to a narrower type).
 __global__ void __launch_bounds__(256)
-syrk_f32_valu(const float* __restrict__ X, int64_t n_tokens, int d, int64_t ldx, int nb, int ntiles,
+syrk_f32_mfma(const float* __restrict__ X, int64_t n_tokens, int d, int64_t ldx, int nb, int ntiles,
               int64_t tokens_per_split, float* __restrict__ partial) {
-  __shared__ float sa[SYF_BK][SYF_T + 4];
-  __shared__ float sb[SYF_BK][SYF_T + 4];
+  __shared__ float sa[SYF_BK][SYF_T];
+  __shared__ float sb[SYF_BK][SYF_T];
   const int tile = blockIdx.x % ntiles;
   const int split = blockIdx.x / ntiles;
   int bi, bj;
@@ -438,9 +445,10 @@ syrk_f32_valu(const float* __restrict__ X, int64_t n_tokens, int d, int64_t ldx,
   const int64_t kbeg = int64_t(split) * tokens_per_split;
   int64_t kend = kbeg + tokens_per_split;
   if (kend > n_tokens) kend = n_tokens;
-  const int tid = threadIdx.x;
-  const int ti = tid >> 4, tj = tid & 15;
-  float acc[4][4] = {};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const int lk = lane >> 5, lc = lane & 31;
+  floatx16 acc = floatx16{0};
   for (int64_t k0 = kbeg; k0 < kend; k0 += SYF_BK) {
     for (int e = tid; e < SYF_BK * SYF_T; e += 256) {
       const int kk = e / SYF_T, c = e % SYF_T;
@@ -450,24 +458,21 @@ syrk_f32_valu(const float* __restrict__ X, int64_t n_tokens, int d, int64_t ldx,
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < SYF_BK; ++kk) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sa[kk][ti * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = sb[kk][tj * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int kk = 0; kk < SYF_BK; kk += 2) {
+      const float a = sa[kk + lk][32 * wi + lc];
+      const float b = sb[kk + lk][32 * wj + lc];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  // 32x32 result layout: lane l holds column l % 32 and rows
+  // 8 (r / 4) + 4 (l / 32) + r % 4 of register r.
   float* out = partial + (int64_t(split) * ntiles + tile) * (SYF_T * SYF_T);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[(ti * 4 + i) * SYF_T + tj * 4 + j] = acc[i][j];
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * wi + 8 * (r >> 2) + 4 * lk + (r & 3);
+    out[row * SYF_T + 32 * wj + lc] = acc[r];
+  }
 }
 
 // H[i][j] = 2 * sum_s partial_s (min(i,j), max(i,j)) (+ H[i][j] if accumulate).
@@ -668,7 +673,7 @@ extern "C" int gptq_hessian_accumulate(const void* X, int xdtype, int64_t n_toke
       if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
     }
   } else {
-    hipLaunchKernelGGL(syrk_f32_valu, dim3(unsigned(int64_t(p.ntiles) * p.nsplit)), dim3(256), 0, s,
+    hipLaunchKernelGGL(syrk_f32_mfma, dim3(unsigned(int64_t(p.ntiles) * p.nsplit)), dim3(256), 0, s,
                        static_cast<const float*>(X), n_tokens, int(d), ldx, p.nb, p.ntiles, p.tokens_per_split,
                        partial);
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;

@@ -7,15 +7,14 @@ run to produce the next block's inputs. Two pieces of that:
 
 * ``quantize_shared_input``: layers that read the same input (the q/k/v
   projections) share one Hessian, accumulated over the calibration chunks
-  (``accumulate``), and one factor; their rows are swept together in one
-  call, since rows are independent given the factor.
+  (``accumulate``), and one factor; each layer is then swept with it, so
+  each layer's loss is the library's own fp64 sum.
 * ``quantize_mlp_block``: up layer, ReLU, down layer, quantized in order,
   the down layer calibrated on the output of the quantized up layer.
 
-Every step of the method runs in the library's kernels. Running the
-quantized layers on the calibration tokens (a [tokens x d_in] x [d_in x d_out]
-product, with the weights dequantized to fp16 by ``gptq_dequantize``) is a
-plain dense GEMM and uses torch's library GEMM; the block's ReLU is torch's.
+Every step runs in the library's kernels, the quantized layers included
+(``gptq_dequant_gemm``: tokens x packed weights on the fp16 MFMA with the
+ReLU in its epilogue). torch only provides device memory and streams.
 """
 
 from __future__ import annotations
@@ -26,7 +25,7 @@ import torch
 
 from . import (
     Quantized,
-    gptq_dequantize,
+    gptq_dequant_gemm,
     gptq_hessian_accumulate,
     gptq_prepare_hinv,
     gptq_quantize_layer,
@@ -36,26 +35,17 @@ from . import (
 def quantize_shared_input(chunks: Iterable[torch.Tensor], Ws: Sequence[torch.Tensor], bits: int, group_size: int,
                           block: int = 128, damp: float = 0.01, symmetric: bool = False):
     """One Hessian over all calibration chunks ([tokens_i, d] each), one
-    factor, and the rows of all layers in ``Ws`` ([rows_k, d] each, one
-    dtype) swept in one call. Returns (H, hinv, stacked Quantized, per-layer
-    list of Quantized views)."""
+    factor, and each layer in ``Ws`` ([rows_k, d] each) swept with it.
+    Returns (H, hinv, list of Quantized, one per layer)."""
     H = None
     for i, X in enumerate(chunks):
         H = gptq_hessian_accumulate(X, H=H, accumulate=i > 0)
     if H is None:
         raise ValueError("no calibration chunks")
     hv = gptq_prepare_hinv(H, damp)
-    W = torch.cat(list(Ws), dim=0)
-    q = gptq_quantize_layer(W, hv.U, bits, group_size, block, symmetric=symmetric)
-    layers: List[Quantized] = []
-    r0 = 0
-    for Wk in Ws:
-        r1 = r0 + Wk.shape[0]
-        rl = q.row_loss[r0:r1]
-        layers.append(Quantized(q.codes[r0:r1], q.scales[r0:r1], q.zeros[r0:r1], q.packed[r0:r1],
-                                rl.double().sum(), rl))
-        r0 = r1
-    return H, hv, q, layers
+    layers: List[Quantized] = [gptq_quantize_layer(Wk, hv.U, bits, group_size, block, symmetric=symmetric)
+                               for Wk in Ws]
+    return H, hv, layers
 
 
 def quantize_mlp_block(X0: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tensor, bits: int, group_size: int,
@@ -70,12 +60,9 @@ def quantize_mlp_block(X0: torch.Tensor, W_up: torch.Tensor, W_down: torch.Tenso
     H_up = gptq_hessian_accumulate(X0)
     hv_up = gptq_prepare_hinv(H_up, damp)
     q_up = gptq_quantize_layer(W_up, hv_up.U, bits, group_size, block)
-    Wh_up = gptq_dequantize(q_up.packed, q_up.scales, q_up.zeros, d_model, bits, group_size, torch.float16)
-    X1 = torch.matmul(X0, Wh_up.t())
-    X1.relu_()
+    X1 = gptq_dequant_gemm(q_up.packed, q_up.scales, q_up.zeros, d_model, bits, group_size, X0, relu=True)
     H_down = gptq_hessian_accumulate(X1)
     hv_down = gptq_prepare_hinv(H_down, damp)
     q_down = gptq_quantize_layer(W_down, hv_down.U, bits, group_size, block)
-    Wh_down = gptq_dequantize(q_down.packed, q_down.scales, q_down.zeros, d_ff, bits, group_size, torch.float16)
-    X2 = torch.matmul(X1, Wh_down.t())
+    X2 = gptq_dequant_gemm(q_down.packed, q_down.scales, q_down.zeros, d_ff, bits, group_size, X1)
     return dict(H_up=H_up, hinv_up=hv_up, up=q_up, X1=X1, H_down=H_down, hinv_down=hv_down, down=q_down, X2=X2)

@@ -129,7 +129,9 @@ def check_quant(t: LayerOutputs, ref: dict, bits: int, rerun: Callable, *, tie: 
     """Check the tested rows against the oracle (module docstring). Returns
     a summary: codes matching the oracle's own rows, rows that needed
     flips, flips in total, the largest code difference against the
-    oracle's own rows, and the match against the followed continuations."""
+    oracle's own rows, the match against the followed continuations, and
+    ``matched``: the oracle rows each tested row was matched with (codes,
+    scales, zeros, row_loss; all values the oracle computed)."""
     codes = np.asarray(t.codes)
     zeros = np.asarray(t.zeros).astype(np.int64)
     scales = np.asarray(t.scales, dtype=np.float64)
@@ -147,8 +149,11 @@ def check_quant(t: LayerOutputs, ref: dict, bits: int, rerun: Callable, *, tie: 
     flipped_rows, n_flips = 0, 0
     matched_equal = 0
     worst_scale = 0.0
+    matched = {k: np.array(ref[k], copy=True) for k in ("codes", "scales", "zeros", "row_loss")}
     for i in range(n_rows):
         r, flips = follow_row(codes[i], zeros[i], _row(ref, i), rerun, i, tie, max_flips_per_row)
+        for k in matched:
+            matched[k][i] = r[k]
         if flips:
             flipped_rows += 1
             n_flips += len(flips)
@@ -177,7 +182,7 @@ def check_quant(t: LayerOutputs, ref: dict, bits: int, rerun: Callable, *, tie: 
         raise ParityError(f"loss {lt:.6g} against the oracle's {lref:.6g}")
     summary = dict(rows=n_rows, match_oracle=match0, max_abs_diff_oracle=int(np.abs(diff0).max(initial=0)),
                    flipped_rows=flipped_rows, flips=n_flips, match_followed=match, worst_scale_rel=worst_scale,
-                   loss=lt, loss_oracle=lref)
+                   loss=lt, loss_oracle=lref, matched=matched)
     if log:
         log(f"  parity{(' ' + label) if label else ''}: {n_rows} rows; codes equal to the oracle's own rows "
             f"{match0:.6f} (max |diff| {summary['max_abs_diff_oracle']}); rows followed through near-tie flips "

@@ -1,0 +1,102 @@
+"""The quantized layer run on token batches (gptq_dequant_gemm) against the
+oracle's run_quantized_layer (needs an MI355X).
+
+Both sides use the same fp16 weights s (code - z) (the fp32 product rounded
+to fp16), products of fp16 values are exact, and the oracle sums in float64.
+The kernel sums K = d_in products in fp32 in the MFMA's order, which moves
+the sum by at most (K + 2) 2^-24 sum |x w| before the final rounding to
+fp16; rounding is monotone, so every output must lie between the fp16
+roundings of (exact - bound) and (exact + bound), ReLU applied to both. Most
+outputs equal the oracle's fp16 value exactly (counted and bounded below).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gptq_oracle as O
+from tests.test_gpu_parity import DEV, gpu_tensor, say
+
+pytestmark = pytest.mark.gpu
+
+
+def layer(d_out, d_in, bits, group, seed):
+    r = np.random.default_rng(seed)
+    ng = 1 if group == -1 else -(-d_in // group)
+    codes = r.integers(0, 1 << bits, size=(d_out, d_in))
+    scales = r.uniform(0.001, 0.03, size=(d_out, ng)).astype(np.float32)
+    zeros = r.integers(0, 1 << bits, size=(d_out, ng)).astype(np.int32)
+    return O.pack(codes, bits), scales, zeros
+
+
+def tokens(n, d_in, seed):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((n, d_in)).astype(np.float32)
+    x[:, r.choice(d_in, max(1, d_in // 100), replace=False)] *= 20.0
+    return x.astype(np.float16)
+
+
+def check_gemm(y, X, packed, scales, zeros, d_in, bits, group, relu):
+    Wh = O.model_weight_f16(O.unpack(packed, d_in, bits), scales, zeros, group).astype(np.float64)
+    Xd = X.astype(np.float64)
+    exact = Xd @ Wh.T
+    bound = (d_in + 2) * 2.0**-24 * (np.abs(Xd) @ np.abs(Wh).T)
+    lo, hi = exact - bound, exact + bound
+    if relu:
+        lo, hi = np.maximum(lo, 0.0), np.maximum(hi, 0.0)
+    lo16, hi16 = lo.astype(np.float16).astype(np.float64), hi.astype(np.float16).astype(np.float64)
+    g = y.astype(np.float64)
+    ok = (g >= lo16) & (g <= hi16)
+    assert ok.all(), f"{int((~ok).sum())} outputs outside the fp32-summation bound"
+    ref = O.run_quantized_layer(X, packed, scales, zeros, d_in, bits, group, relu)
+    same = float(np.mean(y.astype(np.float64) == ref.astype(np.float64)))
+    say(f"  gemm: {y.size} outputs within the bound; equal to the oracle's fp16 value {same:.6f}")
+    assert same >= 0.99
+    return same
+
+
+@pytest.mark.parametrize("n,d_out,d_in,bits,group,relu", [
+    (1, 1, 64, 4, -1, False),
+    (300, 200, 128, 4, 128, True),
+    (1000, 130, 256, 3, -1, False),
+    (77, 257, 192, 2, 64, True),
+    (513, 384, 512, 8, 128, False),
+    (4096, 1376, 512, 4, 128, True),
+    (257, 129, 1408, 3, 128, True),
+    (300, 70, 1376, 4, -1, False),  # d_in = 43 x 32: a last K tile of 32 columns
+    (129, 33, 96, 2, -1, True),
+])
+def test_dequant_gemm_parity(gpu, n, d_out, d_in, bits, group, relu):
+    say("dequant gemm", n, d_out, d_in, bits, group, relu)
+    packed, scales, zeros = layer(d_out, d_in, bits, group, n + d_out)
+    X = tokens(n, d_in, d_in + bits)
+    y = gpu.gptq_dequant_gemm(gpu_tensor(packed.view(np.int32)), gpu_tensor(scales), gpu_tensor(zeros), d_in, bits,
+                              group, gpu_tensor(X), relu=relu)
+    torch.cuda.synchronize()
+    check_gemm(y.cpu().numpy(), X, packed, scales, zeros, d_in, bits, group, relu)
+
+
+def test_dequant_gemm_strided_and_bad_arguments(gpu):
+    """Strided X and Y rows (views), nothing written past d_out, no tokens,
+    and the argument checks."""
+    n, d_out, d_in, bits, group = 300, 96, 256, 4, 64
+    packed, scales, zeros = layer(d_out, d_in, bits, group, 5)
+    X = tokens(n, d_in, 6)
+    Xbig = gpu_tensor(np.concatenate([X, np.ones((n, 64), np.float16)], axis=1))
+    Ybig = torch.full((n, d_out + 40), -7.0, dtype=torch.float16, device=DEV)
+    P, S, Z = gpu_tensor(packed.view(np.int32)), gpu_tensor(scales), gpu_tensor(zeros)
+    gpu.gptq_dequant_gemm(P, S, Z, d_in, bits, group, Xbig[:, :d_in], Y=Ybig[:, :d_out])
+    torch.cuda.synchronize()
+    yb = Ybig.cpu().numpy()
+    check_gemm(yb[:, :d_out], X, packed, scales, zeros, d_in, bits, group, False)
+    assert np.all(yb[:, d_out:] == -7.0)
+    e = gpu.gptq_dequant_gemm(P, S, Z, d_in, bits, group, Xbig[:0, :d_in])
+    assert e.shape == (0, d_out)
+    lib = gpu.load()
+    p = Ybig.data_ptr()
+    x = Xbig.data_ptr()
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 100, 4, -1, x, 4, 320, p, 8, 0, None) == gpu.GPTQ_E_UNSUPPORTED  # d_in % 32
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, 32, x, 4, 320, p, 8, 0, None) == gpu.GPTQ_E_UNSUPPORTED  # group
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 5, -1, x, 4, 320, p, 8, 0, None) == gpu.GPTQ_E_INVALID_ARG  # bits
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 100, p, 8, 0, None) == gpu.GPTQ_E_INVALID_ARG  # ldx
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 320, p, 8, 2, None) == gpu.GPTQ_E_INVALID_ARG  # relu

@@ -417,3 +417,21 @@ def test_brute_force_catches_planted_mistakes():
         same = np.array_equal(out["codes"], codes) and np.allclose(out["Wq"], Wq, atol=1e-12)
         loss_ok = abs(out["loss"] - O.layer_loss_direct(X, W, out["Wq"], lam)) < 1e-10 * max(1.0, out["loss"])
         assert not (same and loss_ok), name
+
+
+def test_run_quantized_layer_hand_example():
+    # 2-bit codes [[1, 2], [3, 0]], one group per row, s = [0.5, 0.25], z = [1, 2]:
+    # What = [[0, 0.5], [0.25, -0.5]]. X = [[2, 4], [1, -1]]:
+    # X What^T = [[2, -1.5], [-0.5, 0.75]]; with ReLU [[2, 0], [0, 0.75]].
+    packed = O.pack(np.array([[1, 2], [3, 0]]), 2)
+    scales = np.array([[0.5], [0.25]], np.float32)
+    zeros = np.array([[1], [2]])
+    X = np.array([[2, 4], [1, -1]], np.float16)
+    y = O.run_quantized_layer(X, packed, scales, zeros, 2, 2, -1)
+    assert y.dtype == np.float16 and y.tolist() == [[2.0, -1.5], [-0.5, 0.75]]
+    assert O.run_quantized_layer(X, packed, scales, zeros, 2, 2, -1, relu=True).tolist() == [[2.0, 0.0], [0.0, 0.75]]
+    # the sum is rounded to fp16 once: 1 + 2^-11 + 2^-11 is exactly 1 + 2^-10
+    packed = O.pack(np.array([[1, 1, 1]]), 2)
+    X = np.array([[1.0, 2.0**-11, 2.0**-11]], np.float16)
+    y = O.run_quantized_layer(X, packed, np.ones((1, 1), np.float32), np.zeros((1, 1)), 3, 2, -1)
+    assert float(y[0, 0]) == 1.0 + 2.0**-10
