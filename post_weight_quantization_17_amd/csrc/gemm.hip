@@ -7,8 +7,8 @@
 // the fly. What = s (code - z) per group (astro-blog survey, section 1.2),
 // held as fp16 to run: the fp32 product s (code - z), rounded to fp16.
 //
-// Design (gfx950), one workgroup of 4 waves per 256-token x 128-weight-row
-// output tile, K (d_in) in tiles of 64:
+// Design (gfx950), one workgroup of 8 waves (two per SIMD) per 256-token x
+// 128-weight-row output tile, K (d_in) in tiles of 64:
 //  * X tiles [256 tokens][64] fp16 go through registers into LDS (row pitch
 //    72 halfs, so the 16-byte fragment reads of 32 consecutive rows fall on
 //    distinct banks).
@@ -34,7 +34,8 @@ constexpr int G_BM = 256;          // tokens per tile
 constexpr int G_BN = 128;          // weight rows per tile
 constexpr int G_BK = 64;           // K per tile
 constexpr int G_P = G_BK + 8;      // LDS row pitch (halfs)
-constexpr int G_THREADS = 256;
+constexpr int G_THREADS = 512;      // 8 waves, two per SIMD
+constexpr int G_XS = 3;            // X stages in LDS
 
 // Code j (0..31) of a unit of BITS words: bits [BITS j, BITS j + BITS) of
 // the unit's LSB-first stream.
@@ -64,11 +65,12 @@ __device__ __forceinline__ uint32_t dq_pair(const uint32_t (&w)[BITS], float s, 
   return dq_half(unit_field<BITS, J>(w), s, zoff) | (dq_half(unit_field<BITS, J + 1>(w), s, zoff) << 16);
 }
 
-template <int BITS, int J = 0>
-__device__ __forceinline__ void static_for_pairs(const uint32_t (&w)[BITS], float s, float zoff, uint32_t (&h)[16]) {
-  if constexpr (J < 32) {
-    h[J / 2] = dq_pair<BITS, J>(w, s, zoff);
-    static_for_pairs<BITS, J + 2>(w, s, zoff, h);
+// Codes H * 16 + 2 i, + 1 (i < 8) of a unit, as 8 pairs of fp16 bits.
+template <int BITS, int H, int I = 0>
+__device__ __forceinline__ void half_unit_pairs(const uint32_t (&w)[BITS], float s, float zoff, uint32_t (&h)[8]) {
+  if constexpr (I < 8) {
+    h[I] = dq_pair<BITS, 16 * H + 2 * I>(w, s, zoff);
+    half_unit_pairs<BITS, H, I + 1>(w, s, zoff, h);
   }
 }
 
@@ -77,108 +79,164 @@ __global__ void __launch_bounds__(G_THREADS, 1)
 dequant_gemm_f16(const uint32_t* __restrict__ packed, const float* __restrict__ scales,
                  const int32_t* __restrict__ zeros, int d_out, int d_in, int nwords, int group, int ngroups,
                  const __half* __restrict__ X, int64_t n_tok, int64_t ldx, __half* __restrict__ Y, int64_t ldy,
-                 int relu, int n_tiles_n) {
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][G_BM * G_P];
-  __shared__ __attribute__((aligned(16))) _Float16 ws[2][G_BN * G_P];
+                 int relu, int n_tiles_n, int n_tiles_m8) {
+  // X: G_XS stages of [256 rows][128 bytes], 16-byte chunk c of row r at
+  // slot c ^ (r & 7) (the fragment reads of 32 consecutive rows then spread
+  // over the banks). W: two stages of the dequantized tile, row pitch G_P.
+  __shared__ __attribute__((aligned(16))) unsigned char xs[G_XS][G_BM * 128];
+  __shared__ __attribute__((aligned(16))) _Float16 ws0[G_BN * G_P];
+  __shared__ __attribute__((aligned(16))) _Float16 ws1[G_BN * G_P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  // consecutive workgroups share the token tile and sweep the weight tiles
-  const int tn = int(blockIdx.x % unsigned(n_tiles_n));
-  const int64_t tm = int64_t(blockIdx.x / unsigned(n_tiles_n));
+  const int wm = wave >> 1, wn = wave & 1;  // wave tile: tokens 64 wm .., rows 64 wn ..
+  // Workgroups go to the 8 XCDs round-robin (b % 8). When the token tiles
+  // split evenly, XCD x takes token tiles x, x + 8, ..., each across all
+  // weight tiles in turn, so the X tile its CUs share stays in its own L2;
+  // otherwise consecutive workgroups share the token tile.
+  int tn;
+  int64_t tm;
+  const unsigned b = blockIdx.x;
+  if (n_tiles_m8) {
+    const unsigned j = b >> 3;
+    tm = int64_t(j / unsigned(n_tiles_n)) * 8 + (b & 7);
+    tn = int(j % unsigned(n_tiles_n));
+  } else {
+    tn = int(b % unsigned(n_tiles_n));
+    tm = int64_t(b / unsigned(n_tiles_n));
+  }
   const int64_t m0 = tm * G_BM;
   const int n0 = tn * G_BN;
   const int nkt = (d_in + G_BK - 1) / G_BK;  // d_in % 32 == 0: the last tile may hold 32 columns
 
-  // X loads: 8 per thread per tile, lane group of 8 covers one row's 128 bytes.
-  const int xr = tid >> 3, xc = (tid & 7) * 8;  // row (of 32) and K offset
-  const __half* xrow[8];
+  // Direct X loads: instruction i of wave w fills rows 8 (w + 8 i) .. + 7 of
+  // a stage (1 KB); lane l brings row 8 (w + 8 i) + l / 8, logical chunk
+  // (l % 8) ^ (row & 7), which lands in slot l % 8.
+  constexpr int XL = G_BM * 128 / (16 * G_THREADS);  // direct loads per thread per tile
+  const __half* xsrc[XL];
+  int xchunk[XL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int64_t t = m0 + xr + 32 * i;
+  for (int i = 0; i < XL; ++i) {
+    const int r = 8 * (wave + 8 * i) + (lane >> 3);
+    int64_t t = m0 + r;
     if (t >= n_tok) t = n_tok - 1;  // clamped rows are computed and never stored
-    xrow[i] = X + t * ldx + xc;
+    xchunk[i] = (lane & 7) ^ (r & 7);
+    xsrc[i] = X + t * ldx + 8 * xchunk[i];
   }
-  // W unit: row wr of the tile, unit wu (codes 32 wu .. 32 wu + 31 of the K tile).
-  const int wr = tid >> 1, wu = tid & 1;
+  auto issue_x = [&](int kt, int st) {
+    const int k0 = kt * G_BK;
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      // In a last tile of 32 columns, chunks past d_in re-read chunks 0-3 of
+      // the row (their weights are zero, so they add nothing).
+      const int kc = k0 + 8 * xchunk[i] < d_in ? k0 : k0 - 32;
+      __builtin_amdgcn_global_load_lds(xsrc[i] + kc,
+                                       (__attribute__((address_space(3))) void*)(xs[st] + 1024 * (wave + 8 * i)), 16,
+                                       0, 0);
+    }
+  };
+  // Dequantization: the 256 units of a K tile (row wr, unit wu) are split in
+  // halves of 16 codes; waves 0-3 take the first halves, waves 4-7 the second
+  // (wave-uniform, so the bit offsets are compile-time constants).
+  const int uidx = tid & 255, hh = wave >> 2;
+  const int wr = uidx >> 1, wu = uidx & 1;
   const int wrow = n0 + wr < d_out ? n0 + wr : d_out - 1;
   const uint32_t* prow = packed + size_t(wrow) * nwords;
   const float* srow = scales + size_t(wrow) * ngroups;
   const int32_t* zrow = zeros + size_t(wrow) * ngroups;
-
-  uint4 xv[8];
-  uint32_t pw[BITS];
-  float sv = 0.f, zoff = 0.f;
-  auto load_tile = [&](int kt) {
+  struct Unit {
+    uint32_t w[BITS];
+    float s, zoff;
+  };
+  auto load_unit = [&](int kt, Unit& u) {
     const int k0 = kt * G_BK;
-    // In a last tile of 32 columns, the second half of X and the second
-    // unit are zeros (nothing past d_in is read); their products add 0.
-    const bool x_in = k0 + xc < d_in, w_in = k0 + 32 * wu < d_in;
+    const bool in = k0 + 32 * wu < d_in;  // the second unit of a last 32-column tile is zero
+    const int unit = (k0 >> 5) + (in ? wu : 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      xv[i] = x_in ? *reinterpret_cast<const uint4*>(xrow[i] + k0) : make_uint4(0u, 0u, 0u, 0u);
-    const int unit = (k0 >> 5) + wu;
-#pragma unroll
-    for (int b = 0; b < BITS; ++b) pw[b] = w_in ? prow[unit * BITS + b] : 0u;
-    const int g = (group > 0 && w_in) ? (k0 + 32 * wu) / group : 0;
-    sv = w_in ? srow[g] : 0.f;
-    zoff = 8388608.f + (w_in ? float(zrow[g]) : 0.f);
+    for (int b = 0; b < BITS; ++b) u.w[b] = prow[unit * BITS + b];
+    const int g = group > 0 ? (32 * unit) / group : 0;
+    u.s = in ? srow[g] : 0.f;
+    u.zoff = 8388608.f + float(zrow[g]);
   };
-  auto store_tile = [&](int st) {
-    _Float16* xd = xs[st];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(xd + (xr + 32 * i) * G_P + xc) = xv[i];
-    uint32_t h[16];
-    static_for_pairs<BITS>(pw, sv, zoff, h);
-    _Float16* wd = ws[st] + wr * G_P + 32 * wu;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<uint4*>(wd + 8 * q) = make_uint4(h[4 * q], h[4 * q + 1], h[4 * q + 2], h[4 * q + 3]);
+  auto store_unit = [&](const Unit& u, _Float16* wst) {
+    uint32_t h[8];
+    if (hh == 0)
+      half_unit_pairs<BITS, 0>(u.w, u.s, u.zoff, h);
+    else
+      half_unit_pairs<BITS, 1>(u.w, u.s, u.zoff, h);
+    _Float16* wd = wst + wr * G_P + 32 * wu + 16 * hh;
+    *reinterpret_cast<uint4*>(wd) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(wd + 8) = make_uint4(h[4], h[5], h[6], h[7]);
   };
 
-  floatx16 acc[4][2];
+  floatx16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{0};
 
-  // fragment bases: lane l reads row l % 32 of its tile, K 8 (l / 32) ..
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) load_tile(kt + 1);
-    const _Float16* xa = xs[st] + (wm * 128 + fr) * G_P + fk;
-    const _Float16* wb = ws[st] + (wn * 64 + fr) * G_P + fk;
+  // fragment reads: lane l takes row l % 32 of its 32-row tile and logical
+  // chunk l / 32 + 2 kk of the K tile (8 consecutive K)
+  const int fr = lane & 31, fh = lane >> 5;
+  auto mma = [&](int st, const _Float16* wst) {
+    const unsigned char* xa = xs[st];
+    const _Float16* wb = wst + (wn * 64 + fr) * G_P + 8 * fh;
 #pragma unroll
     for (int kk = 0; kk < G_BK / 16; ++kk) {
-      half8 a[4], b[2];
+      half8 a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const half8*>(xa + 32 * i * G_P + 16 * kk);
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + 32 * i + fr;
+        a[i] = *reinterpret_cast<const half8*>(xa + r * 128 + 16 * ((fh + 2 * kk) ^ (r & 7)));
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const half8*>(wb + 32 * j * G_P + 16 * kk);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (more) store_tile(st ^ 1);
-    __syncthreads();
+  };
+
+  // Schedule (per thread, VMEM ops in issue order): prologue W(0) X(0) W(1)
+  // X(1); iteration kt issues W(kt+2) then X(kt+2) after its barrier. So at
+  // iteration kt the XL most recent VMEM ops are X(kt+1)'s: vmcnt(XL) means
+  // X(kt) (and W(kt+1)) have landed. Loads past the last tile re-load the
+  // last tile (valid memory, never read), so the count is the same every time.
+  static_assert(XL == 4, "the wait below encodes vmcnt(4)");
+  Unit ua, ub;
+  load_unit(0, ua);
+  issue_x(0, 0);
+  load_unit(nkt > 1 ? 1 : 0, ub);
+  issue_x(nkt > 1 ? 1 : 0, 1 % G_XS);
+  store_unit(ua, ws0);
+  auto step = [&](int kt, Unit& use, Unit& next, _Float16* wcur, _Float16* wnext) {
+    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) expcnt(7) lgkmcnt(0): X(kt) landed, own LDS writes done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int kn = kt + 2 < nkt ? kt + 2 : nkt - 1;
+    load_unit(kn, next);
+    issue_x(kn, (kt + 2) % G_XS);
+    mma(kt % G_XS, wcur);
+    store_unit(use, wnext);  // tile kt + 1 (a last duplicate is written and never read)
+  };
+  int kt = 0;
+  for (; kt + 2 <= nkt; kt += 2) {
+    step(kt, ub, ua, ws0, ws1);
+    step(kt + 1, ua, ub, ws1, ws0);
   }
+  if (kt < nkt) step(kt, ub, ua, ws0, ws1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no direct load outlives the workgroup's LDS
 
   // 32x32 result layout: lane l holds column l % 32 (a weight row) and rows
   // 8 (r / 4) + 4 (l / 32) + r % 4 (tokens) of register r.
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = n0 + wn * 64 + 32 * j + fr;
       if (col >= d_out) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t t = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t t = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * fh + (r & 3);
         if (t >= n_tok) continue;
         float v = acc[i][j][r];
         if (relu) v = v > 0.f ? v : 0.f;
@@ -210,25 +268,26 @@ extern "C" int gptq_dequant_gemm(const uint32_t* packed, const float* scales, co
   const int nwords = int((d_in * bits + 31) / 32);
   const int ngroups = group_size == -1 ? 1 : int((d_in + group_size - 1) / group_size);
   const dim3 grid(unsigned(tiles_m * tiles_n)), block(G_THREADS);
+  const int m8 = tiles_m % 8 == 0 ? 1 : 0;
   hipStream_t s = as_stream(stream);
   const __half* x = static_cast<const __half*>(X);
   __half* y = static_cast<__half*>(Y);
   switch (bits) {
     case 2:
       hipLaunchKernelGGL(dequant_gemm_f16<2>, grid, block, 0, s, packed, scales, zeros, int(d_out), int(d_in), nwords,
-                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n));
+                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n), m8);
       break;
     case 3:
       hipLaunchKernelGGL(dequant_gemm_f16<3>, grid, block, 0, s, packed, scales, zeros, int(d_out), int(d_in), nwords,
-                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n));
+                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n), m8);
       break;
     case 4:
       hipLaunchKernelGGL(dequant_gemm_f16<4>, grid, block, 0, s, packed, scales, zeros, int(d_out), int(d_in), nwords,
-                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n));
+                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n), m8);
       break;
     default:
       hipLaunchKernelGGL(dequant_gemm_f16<8>, grid, block, 0, s, packed, scales, zeros, int(d_out), int(d_in), nwords,
-                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n));
+                         int(group_size), ngroups, x, n_tokens, ldx, y, ldy, relu, int(tiles_n), m8);
       break;
   }
   return launch_status();
