@@ -371,8 +371,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       const float x = row_bcast<o>(wr[m]);
       float c = rintf(div_rn(x, s, rs)) + z;
       c = fminf(fmaxf(c, 0.f), maxq);
-      const float what = s * (c - z);
-      const float err = x - what;
+      const float err = fmaf(-s, c - z, x);  // x - s (c - z), rounded once
       const float e = err * dc;
 #pragma unroll
       for (int mm = m; mm < QM; ++mm) wr[mm] = fmaf(-e, uc[mm], wr[mm]);
@@ -606,10 +605,12 @@ QuantWs carve_q(void* ws, int64_t d_row, int64_t d_col) {
   QuantWs w{};
   const size_t wf = align_up(size_t(d_row) * d_col * sizeof(float), 256);
   const int64_t nwg = (d_row + QR - 1) / QR;
-  char* p = static_cast<char*>(ws);
-  w.Wf = reinterpret_cast<float*>(p);
-  w.wg_loss = reinterpret_cast<double*>(p + wf);
   w.bytes = wf + align_up(size_t(nwg) * sizeof(double), 256);
+  if (ws != nullptr) {  // sizes only when there is no workspace yet
+    char* p = static_cast<char*>(ws);
+    w.Wf = reinterpret_cast<float*>(p);
+    w.wg_loss = reinterpret_cast<double*>(p + wf);
+  }
   return w;
 }
 

@@ -1,0 +1,134 @@
+// Bounds-checked CPU run of the library's column-sweep source
+// (post_weight_quantization_17_amd/csrc/quantize.hip, compiled here against
+// the host emulation headers with AddressSanitizer). Test infrastructure:
+// tests/test_host_emulation.py builds it and compares its outputs with the
+// oracle's.
+//
+//   sweep_host <dir>
+//
+// <dir>/args.txt: wdtype d_row d_col bits group block symmetric mode w_offset
+//   wdtype 0 = fp16, 1 = fp32 weights; mode: "ws" (gptq_quantize_layer with
+//   an exactly sized workspace), "noalloc" (gptq_quantize_layer_noalloc),
+//   or "w1" / "rg2" / "xw2" (the 16-row 4-wave, 32-row and 8-wave whole-tile
+//   instantiations, launched directly on a shape they accept, as the
+//   launcher picks them only for larger layers); w_offset shifts W by that
+//   many elements inside its allocation (0 keeps it 256-byte aligned).
+// <dir>/W.bin (d_row x d_col), <dir>/U.bin (d_col x d_col fp32) in; codes,
+// scales, zeros, packed, row_loss and loss (.bin) out. Every buffer is its
+// own allocation of exactly its size, so any access outside it is reported.
+#include "../../post_weight_quantization_17_amd/csrc/quantize.hip"
+
+#include <fstream>
+#include <string>
+
+namespace {
+
+std::vector<char> slurp(const std::string& path) {
+  std::ifstream f(path, std::ios::binary);
+  return std::vector<char>((std::istreambuf_iterator<char>(f)), std::istreambuf_iterator<char>());
+}
+
+void spill(const std::string& path, const void* p, size_t n) {
+  std::ofstream f(path, std::ios::binary);
+  f.write(static_cast<const char*>(p), std::streamsize(n));
+}
+
+// An allocation of exactly n bytes, 256-byte aligned.
+void* exact(size_t n) {
+  void* p = nullptr;
+  if (posix_memalign(&p, 256, n ? n : 1) != 0) std::abort();
+  return p;
+}
+
+// The whole-tile instantiations that need a large layer to be chosen by the
+// launcher, run directly on a small whole-tile shape (same arguments as the
+// launcher passes them).
+template <typename WT>
+int direct(int rg, int xw, const void* W, int64_t d_row, int64_t d_col, const float* U, int bits, int64_t group,
+           uint8_t* codes, float* scales, int32_t* zeros, uint32_t* packed, double* loss, float* row_loss, void* ws) {
+  using namespace gptq;
+  if (d_col % 64 != 0 || d_row % (rg * QR) != 0) return GPTQ_E_INVALID_ARG;
+  const QuantWs w = carve_q(ws, d_row, d_col);
+  const int ngroups = group == -1 ? 1 : int((d_col + group - 1) / group);
+  const int nwords = int((d_col * bits + 31) / 32);
+  const unsigned nwg = unsigned(d_row / (rg * QR));
+  auto k = rg == 2 ? gptq_sweep<WT, true, 2, 1> : xw == 2 ? gptq_sweep<WT, true, 1, 2> : gptq_sweep<WT, true, 1, 1>;
+  hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * xw * QT), 0, nullptr, static_cast<const WT*>(W), w.Wf, U, int(d_row),
+                     int(d_col), bits, 0, int(group), ngroups, 1, codes, scales, zeros, packed, nwords, row_loss,
+                     w.wg_loss, 128);
+  hipLaunchKernelGGL(loss_final, dim3(1), dim3(256), 0, nullptr, w.wg_loss, int(nwg), loss);
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc != 2) {
+    std::fprintf(stderr, "usage: sweep_host <dir>\n");
+    return 2;
+  }
+  const std::string dir = argv[1];
+  int wdtype, bits, sym, w_offset;
+  long long d_row, d_col, group, block;
+  char mode[16];
+  {
+    FILE* f = std::fopen((dir + "/args.txt").c_str(), "r");
+    if (!f || std::fscanf(f, "%d %lld %lld %d %lld %lld %d %15s %d", &wdtype, &d_row, &d_col, &bits, &group, &block,
+                          &sym, mode, &w_offset) != 9)
+      return 2;
+    std::fclose(f);
+  }
+  const size_t esz = wdtype == GPTQ_F16 ? 2 : 4;
+  const size_t nw = size_t(d_row) * size_t(d_col);
+  const std::vector<char> Wh = slurp(dir + "/W.bin"), Uh = slurp(dir + "/U.bin");
+  if (Wh.size() != nw * esz || Uh.size() != size_t(d_col) * size_t(d_col) * 4) return 2;
+
+  char* Wbase = static_cast<char*>(exact((nw + size_t(w_offset)) * esz));
+  void* W = Wbase + size_t(w_offset) * esz;
+  std::memcpy(W, Wh.data(), Wh.size());
+  float* U = static_cast<float*>(exact(Uh.size()));
+  std::memcpy(U, Uh.data(), Uh.size());
+  const int ng = group == -1 ? 1 : int((d_col + group - 1) / group);
+  const size_t nwords = size_t((d_col * bits + 31) / 32);
+  auto* codes = static_cast<uint8_t*>(exact(nw));
+  auto* scales = static_cast<float*>(exact(size_t(d_row) * ng * 4));
+  auto* zeros = static_cast<int32_t*>(exact(size_t(d_row) * ng * 4));
+  auto* packed = static_cast<uint32_t*>(exact(size_t(d_row) * nwords * 4));
+  auto* row_loss = static_cast<float*>(exact(size_t(d_row) * 4));
+  auto* loss = static_cast<double*>(exact(8));
+
+  const std::string m = mode;
+  int st;
+  if (m == "noalloc") {
+    st = gptq_quantize_layer_noalloc(W, wdtype, d_row, d_col, U, bits, group, block, sym, codes, scales, zeros, packed,
+                                     loss, row_loss, nullptr);
+  } else {
+    const size_t wsb = gptq_quantize_layer_workspace_size(d_row, d_col, bits, group, block);
+    void* ws = exact(wsb);
+    if (m == "ws")
+      st = gptq_quantize_layer(W, wdtype, d_row, d_col, U, bits, group, block, sym, codes, scales, zeros, packed, loss,
+                               row_loss, ws, wsb, nullptr);
+    else if ((m == "w1" || m == "rg2" || m == "xw2") && block == 128 && sym == 0)
+      st = (wdtype == GPTQ_F16 ? direct<__half> : direct<float>)(m == "rg2" ? 2 : 1, m == "xw2" ? 2 : 1, W, d_row,
+                                                                 d_col, U, bits, group, codes, scales, zeros, packed,
+                                                                 loss, row_loss, ws);
+    else
+      st = GPTQ_E_INVALID_ARG;
+    std::free(ws);
+  }
+  if (st != GPTQ_OK) {
+    std::fprintf(stderr, "sweep_host: status %d (%s)\n", st, gptq_status_string(st));
+    return 3;
+  }
+  spill(dir + "/codes.bin", codes, nw);
+  spill(dir + "/scales.bin", scales, size_t(d_row) * ng * 4);
+  spill(dir + "/zeros.bin", zeros, size_t(d_row) * ng * 4);
+  spill(dir + "/packed.bin", packed, size_t(d_row) * nwords * 4);
+  spill(dir + "/row_loss.bin", row_loss, size_t(d_row) * 4);
+  spill(dir + "/loss.bin", loss, 8);
+  for (void* p : {static_cast<void*>(Wbase), static_cast<void*>(U), static_cast<void*>(codes),
+                  static_cast<void*>(scales), static_cast<void*>(zeros), static_cast<void*>(packed),
+                  static_cast<void*>(row_loss), static_cast<void*>(loss)})
+    std::free(p);
+  return 0;
+}

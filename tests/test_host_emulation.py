@@ -1,0 +1,137 @@
+"""The library's column-sweep source run on the CPU with AddressSanitizer and
+UndefinedBehaviorSanitizer (no GPU needed).
+
+tests/host_emulation/ compiles post_weight_quantization_17_amd/csrc/quantize.hip
+for the host against small stand-ins for the HIP runtime: each workgroup runs
+as host threads, the DPP moves and the fp32 MFMA exchange lane values through
+a per-wave buffer, and every buffer the kernels touch is its own exactly
+sized heap allocation. A global access outside any buffer, or undefined
+behaviour in the host or device code, ends the run with a sanitizer report.
+
+Every global address in these kernels is a function of the thread, the
+workgroup and the layer's shape only (no address depends on data), so a
+clean run on a shape shows every access of that shape in bounds. The shapes
+cover each kernel form the launcher picks and the ragged edges: one-column
+and one-row layers, row counts that leave a workgroup partly empty, column
+counts with a partial last block and a partial last 64-column chunk,
+unaligned weights, groups wider than the block, lazy-batch widths below and
+above the block, the symmetric grid, the allocation-free entry point, and
+the whole-tile, 32-row and 8-wave instantiations. The outputs must also pass
+the same oracle parity check as the GPU tests.
+"""
+
+from __future__ import annotations
+
+import hashlib
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+
+import oracle.gptq_oracle as O
+from tests.parity import LayerOutputs, check_quant, rerun_for
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HERE = os.path.join(ROOT, "tests", "host_emulation")
+SRC = os.path.join(ROOT, "post_weight_quantization_17_amd", "csrc")
+CLANG = "/opt/rocm/llvm/bin/clang++"
+FLAGS = ["-std=c++20", "-O0", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+         "-fno-omit-frame-pointer", "-pthread"]
+
+
+def _inputs():
+    files = [os.path.join(HERE, "sweep_main.cpp"), os.path.join(HERE, "hip", "hip_runtime.h"),
+             os.path.join(HERE, "hip", "hip_fp16.h"), os.path.join(SRC, "quantize.hip"),
+             os.path.join(SRC, "gptq_common.h"), os.path.join(ROOT, "include", "gptq_mi355x.h")]
+    h = hashlib.sha256(" ".join(FLAGS).encode())
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+@pytest.fixture(scope="module")
+def sweep_host(tmp_path_factory):
+    if not os.path.exists(CLANG):
+        pytest.skip("ROCm's clang++ is not installed")
+    build = os.path.join(HERE, "_build")
+    os.makedirs(build, exist_ok=True)
+    exe = os.path.join(build, f"sweep_host_{_inputs()}")
+    if not os.path.exists(exe):
+        tmp = exe + ".tmp"
+        r = subprocess.run([CLANG, *FLAGS, "-I", HERE, os.path.join(HERE, "sweep_main.cpp"), "-o", tmp],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-4000:]
+        os.replace(tmp, exe)
+    return exe, tmp_path_factory.mktemp("sweep_host")
+
+
+def _case_inputs(d_row, d_col, bits, wdt):
+    r = np.random.default_rng(d_row * 7919 + d_col)
+    X = r.standard_normal((4 * d_col + 64, d_col)).astype(np.float32)
+    X[:, r.choice(d_col, max(1, d_col // 100), replace=False)] *= 20
+    U = O.prepare_hinv(O.hessian(X), 0.01)[0].astype(np.float32)
+    W = (0.02 * r.standard_normal((d_row, d_col))).astype(wdt)
+    return W, U
+
+
+def _run(exe, work, case):
+    d_row, d_col, bits, group, wdt, opts = case
+    block, sym, mode, off = opts.get("block", 128), opts.get("sym", 0), opts.get("mode", "ws"), opts.get("off", 0)
+    d = os.path.join(str(work), f"{d_row}_{d_col}_{bits}_{group}_{np.dtype(wdt).name}_{block}_{sym}_{mode}_{off}")
+    os.makedirs(d, exist_ok=True)
+    W, U = _case_inputs(d_row, d_col, bits, wdt)
+    W.tofile(os.path.join(d, "W.bin"))
+    U.tofile(os.path.join(d, "U.bin"))
+    with open(os.path.join(d, "args.txt"), "w") as f:
+        f.write(f"{0 if wdt == np.float16 else 1} {d_row} {d_col} {bits} {group} {block} {sym} {mode} {off}\n")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:halt_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    p = subprocess.run([exe, d], capture_output=True, text=True, env=env, timeout=600)
+    return case, d, W, U, p
+
+
+CASES = [
+    (1, 1, 4, -1, np.float32, {}),
+    (5, 7, 3, -1, np.float32, {}),
+    (17, 129, 4, 16, np.float32, {}),
+    (33, 200, 3, 32, np.float16, {}),
+    (20, 300, 2, 64, np.float32, {}),
+    (31, 260, 4, 256, np.float32, {}),
+    (31, 260, 4, 256, np.float32, {"off": 1}),  # unaligned weights: no 16-byte accesses
+    (40, 512, 3, 256, np.float16, {}),
+    (48, 384, 4, 128, np.float32, {"sym": 1}),
+    (31, 260, 4, 256, np.float16, {"off": 3, "mode": "noalloc"}),
+    (33, 300, 4, 16, np.float16, {"block": 256}),  # two-level lazy batches with a ragged tail
+    (33, 300, 4, 16, np.float16, {"block": 32}),
+    (64, 256, 4, 128, np.float16, {}),  # launcher: whole tiles, 8 waves
+    (64, 256, 4, 128, np.float16, {"mode": "w1"}),
+    (64, 512, 3, -1, np.float32, {"mode": "rg2"}),
+    (32, 384, 2, 64, np.float16, {"mode": "xw2"}),
+]
+
+
+def test_sweep_source_runs_in_bounds_under_sanitizers(sweep_host):
+    exe, work = sweep_host
+    with ThreadPoolExecutor(4) as pool:
+        results = list(pool.map(lambda c: _run(exe, work, c), CASES))
+    for case, d, W, U, p in results:
+        d_row, d_col, bits, group, wdt, opts = case
+        assert p.returncode == 0, f"{case}: exit {p.returncode}\n{p.stderr[-6000:]}"
+        ng = 1 if group == -1 else -(-d_col // group)
+        nw = O.words_per_row(d_col, bits)
+
+        def rd(name, dt, shape):
+            return np.fromfile(os.path.join(d, name + ".bin"), dt).reshape(shape)
+
+        out = LayerOutputs(codes=rd("codes", np.uint8, (d_row, d_col)), scales=rd("scales", np.float32, (d_row, ng)),
+                           zeros=rd("zeros", np.int32, (d_row, ng)), packed=rd("packed", np.uint32, (d_row, nw)),
+                           row_loss=rd("row_loss", np.float32, (d_row,)))
+        block, sym = opts.get("block", 128), bool(opts.get("sym", 0))
+        ref = O.quantize_layer(W, U, bits, group, block, decide=np.float32, symmetric=sym)
+        check_quant(out, ref, bits, rerun_for(W, U, bits, group, block, symmetric=sym), label=str(case), log=None)
+        loss = float(rd("loss", np.float64, (1,))[0])
+        assert loss == pytest.approx(float(out.row_loss.astype(np.float64).sum()), rel=1e-6)
+    shutil.rmtree(str(work), ignore_errors=True)
