@@ -53,6 +53,8 @@ constexpr int RG2_MIN_COLS = 12288;
 constexpr int XW2_MAX_WG = 256;
 // Largest lazy-batch width (a multiple of QB) the sweep takes.
 constexpr int LZ_MAX_B = 1024;
+// Blocks per super-block of the 32-row and 8-wave whole-tile forms.
+constexpr int SUPER_BLOCKS = 4;
 
 template <int Q, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -74,6 +76,19 @@ __device__ __forceinline__ floatx4 load4(const __half* p) {
   const __half2 a = *reinterpret_cast<const __half2*>(&v.x);
   const __half2 b = *reinterpret_cast<const __half2*>(&v.y);
   return floatx4{__low2float(a), __high2float(a), __low2float(b), __high2float(b)};
+}
+
+// Buffer-resource loads: a uniform base and size in a 4-SGPR descriptor, a
+// 32-bit per-lane byte offset in one VGPR and a uniform byte offset in an
+// SGPR. The deferred update reads U this way, so no 64-bit per-lane address
+// occupies registers while its loads are in flight (its deep ring of U
+// loads needs the room). Every offset used stays inside the size given.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ floatx4 bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
 // Grid of one group from its range [mn, mx] (which always includes 0).
@@ -110,47 +125,60 @@ __device__ __forceinline__ float div_rn(float x, float s, float rs) {
   return fmaf(r, rs, q);
 }
 
-// Whole-tile form of the deferred update W[rows, i2:] -= E U[i1:i2, i2:]
-// (i2 = i1 + QB), used when the layer needs no bounds test anywhere:
-// d_col % 64 == 0, d_row a multiple of the workgroup's rows, W and U 16-byte
-// aligned. The workgroup's rows are RG v_mfma_f32_16x16x4f32 M tiles of 16
-// rows (Es the A operand) and U rows i1.. the B operand; wave w of the
-// NW = 4 RG XW waves takes the 64-column chunks i2 + 64 w + 64 NW c and
-// applies all RG M tiles to each U operand it loads, so the U traffic per
-// row falls with RG (XW > 1 only adds waves to this update). With no branches in the loop, the next chunk's W tiles (the
-// accumulators' start values) and the U rows RING k-steps ahead, across
-// chunk boundaries, stay in flight while the current chunk's MFMAs run.
-template <typename WT, int RG, int XW>
+// Whole-tile form of a deferred update W[rows, n_lo:n_hi] -= E[:, ec0:ec0+K]
+// U[k0:k0+K, n_lo:n_hi], K = 128 nkb, used when the layer needs no bounds
+// test anywhere: d_col % 64 == 0, d_row a multiple of the workgroup's rows,
+// W and U 16-byte aligned. The workgroup's rows are RG v_mfma_f32_16x16x4f32
+// M tiles of 16 rows (Es the A operand) and U rows k0.. the B operand; wave w
+// of the NW = 4 RG XW waves takes the 64-column chunks n_lo + 64 w + 64 NW c
+// and applies all RG M tiles to each U operand it loads, so the U traffic per
+// row falls with RG (XW > 1 only adds waves to this update). Each chunk of W
+// is read once and written once per call, whatever K is. With no branches
+// in the loop, the next chunk's W tiles (the accumulators' start values) and
+// the U rows RING k-steps ahead, across chunk boundaries, stay in flight
+// while the current chunk's MFMAs run.
+template <typename WT, int RG, int XW, int EP>
 __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, float* __restrict__ Wf,
-                                                      const float* __restrict__ U, const float (*Es)[QB + 4],
-                                                      int d_col, int row0, int i1, bool first) {
+                                                      const float* __restrict__ U, const float (*Es)[EP], int d_col,
+                                                      int row0, int n_lo, int n_hi, int k0, int ec0, int nkb,
+                                                      bool first) {
   constexpr int NW = 4 * RG * XW;  // waves per workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lk = lane >> 4;
-  const int nb0 = i1 + QB + 64 * wave;
-  const int nch = nb0 < d_col ? (d_col - nb0 + 64 * NW - 1) / (64 * NW) : 0;
-  const size_t ustep = size_t(4) * d_col;
-  const float* __restrict__ ub = U + size_t(i1 + lk) * d_col + nb0 + 4 * li;
-  size_t wrow[RG];
-#pragma unroll
-  for (int g = 0; g < RG; ++g) wrow[g] = size_t(row0 + 16 * g + 4 * lk) * d_col + nb0 + 4 * li;
-  auto ldb = [&](int ch, int t) -> floatx4 { return load4(ub + 64 * NW * ch + t * ustep); };
+  const int nb0 = n_lo + 64 * wave;
+  const int nch = nb0 < n_hi ? (n_hi - nb0 + 64 * NW - 1) / (64 * NW) : 0;
+  // U rows k0 .. k0 + 128 nkb as one buffer (byte offsets relative to row
+  // k0); W and Wf through plain pointers, element offsets relative to the
+  // workgroup's first row.
+  const rsrc_t ur = make_rsrc(U + size_t(k0) * d_col, uint32_t(QB * nkb) * uint32_t(d_col) * 4u);
+  const uint32_t col = uint32_t(nb0 + 4 * li);
+  const uint32_t uv = (uint32_t(lk) * uint32_t(d_col) + col) * 4u;  // U row lk, column col
+  const uint32_t ustep = 16u * uint32_t(d_col);                       // bytes per k-step (4 U rows)
+  const uint32_t chb = 64u * NW * 4u;                                 // U bytes per chunk step
+  const float* __restrict__ eb = &Es[li][ec0 + lk];  // A operand of k-step T: eb[16 g EP + 4 T]
+  auto ldb = [&](int ch, int T) -> floatx4 { return bload4(ur, uv, uint32_t(ch) * chb + uint32_t(T) * ustep); };
+  // (the workgroup's 16 RG rows span fewer than 2^32 elements: d_col <= 2^20)
+  const WT* __restrict__ w0 = W + size_t(row0) * d_col;
+  float* __restrict__ f0 = Wf + size_t(row0) * d_col;
+  const uint32_t wv = uint32_t(4 * lk) * uint32_t(d_col) + col;  // element of row 4 lk, column col
+  // rows 16 g + 4 lk + r of chunk ch: element wv + (16 g + r) d_col + 64 NW ch
+  auto wso = [&](int g, int r, int ch) {
+    return wv + uint32_t(16 * g + r) * uint32_t(d_col) + uint32_t(64 * NW * ch);
+  };
   auto ldw = [&](int ch, floatx4 (&v)[RG][4]) {
 #pragma unroll
     for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const size_t off = wrow[g] + size_t(r) * d_col + 64 * NW * ch;
-        v[g][r] = first ? load4(W + off) : load4(Wf + off);
-      }
+      for (int r = 0; r < 4; ++r) v[g][r] = first ? load4(w0 + wso(g, r, ch)) : load4(f0 + wso(g, r, ch));
   };
   // U k-steps in flight. RG = 2 reads its A operands from LDS one k-step
   // ahead instead of keeping all 64 of them in registers, which leaves room
   // for a deeper ring.
   constexpr int RING = RG == 1 ? 8 : sizeof(WT) == 2 ? 16 : 8;
-  constexpr int KS4 = QB / 4;             // k-steps per chunk
-  // Step t of a chunk uses slot t % RING, and the last RING steps prefetch
-  // the next chunk's first steps into their own slots: RING must divide KS4.
+  constexpr int KS4 = QB / 4;             // k-steps per 128 rows of U
+  // Step t of a 32-step group uses slot t % RING, and the last RING steps of
+  // a chunk prefetch the next chunk's first steps into their own slots: RING
+  // must divide KS4.
   static_assert(KS4 % RING == 0, "the ring's slots must line up across chunks");
   floatx4 ring[RING];
   floatx4 wn[RG][4];
@@ -172,41 +200,48 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
     float an[RG];  // RG = 2: the next k-step's A operands
     if constexpr (RG > 1) {
 #pragma unroll
-      for (int g = 0; g < RG; ++g) an[g] = -Es[16 * g + li][lk];
+      for (int g = 0; g < RG; ++g) an[g] = -eb[16 * g * EP];
     }
+    // One group of KS4 k-steps (128 rows of U). In every group but the
+    // chunk's last, all prefetches stay in this chunk.
+    auto group = [&](int kb, bool last) {
 #pragma unroll
-    for (int t = 0; t < KS4; ++t) {
-      const floatx4 b = ring[t % RING];
-      if (t + RING < KS4)
-        ring[t % RING] = ldb(ch, t + RING);
-      else if (more)
-        ring[t % RING] = ldb(ch + 1, t + RING - KS4);
-      if constexpr (RG == 1) {
-        const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
+      for (int t = 0; t < KS4; ++t) {
+        const int T = KS4 * kb + t;
+        const floatx4 b = ring[t % RING];
+        if (!last || t + RING < KS4)
+          ring[t % RING] = ldb(ch, T + RING);
+        else if (more)
+          ring[t % RING] = ldb(ch + 1, t + RING - KS4);
+        if constexpr (RG == 1) {
+          const float at = -eb[4 * T];  // A operand: row li, k = 4T + lk
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[0][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[0][v], 0, 0, 0);
-      } else {
-        float a[RG];
+          for (int v = 0; v < 4; ++v) acc[0][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[0][v], 0, 0, 0);
+        } else {
+          float a[RG];
 #pragma unroll
-        for (int g = 0; g < RG; ++g) a[g] = an[g];
-        if (t + 1 < KS4) {
+          for (int g = 0; g < RG; ++g) a[g] = an[g];
+          if (!last || t + 1 < KS4) {
 #pragma unroll
-          for (int g = 0; g < RG; ++g) an[g] = -Es[16 * g + li][4 * (t + 1) + lk];
+            for (int g = 0; g < RG; ++g) an[g] = -eb[16 * g * EP + 4 * (T + 1)];
+          }
+          asm volatile("" ::: "memory");  // each step's reads stay in their step (no hoisting)
+#pragma unroll
+          for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[g][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g], b[v], acc[g][v], 0, 0, 0);
         }
-        asm volatile("" ::: "memory");  // each step's reads stay in their step (no hoisting)
-#pragma unroll
-        for (int g = 0; g < RG; ++g)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[g][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[g], b[v], acc[g][v], 0, 0, 0);
       }
-    }
+    };
+    for (int kb = 0; kb + 1 < nkb; ++kb) group(kb, false);
+    group(nkb - 1, true);
 #pragma unroll
     for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const size_t off = wrow[g] + size_t(r) * d_col + 64 * NW * ch;
-        *reinterpret_cast<float4*>(Wf + off) = make_float4(acc[g][0][r], acc[g][1][r], acc[g][2][r], acc[g][3][r]);
-      }
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<float4*>(f0 + wso(g, r, ch)) =
+            make_float4(acc[g][0][r], acc[g][1][r], acc[g][2][r], acc[g][3][r]);
   }
 }
 
@@ -226,7 +261,18 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
 // those widths run the LZ = 0 form. Each element sees the same fp32
 // operations in the same order for every B, so every B gives the same
 // results to the bit, as the method's exact lazy batches promise.
-template <typename WT, bool WHOLE, int RG, int XW, int LZ = 0>
+//
+// SB > 1 (whole-tile form, B = QB, groups of at most QB columns) applies the
+// same two-level deferral inside the kernel with SB-block super-blocks: the
+// columns past a super-block receive its SB QB errors in one K = SB QB pass,
+// so the fp32 working copy of those columns is read and written once per
+// super-block instead of once per block. Each element still receives the
+// errors block by block in column order (the MFMA chain over K runs in that
+// order and W's fp32 value is exact in memory between blocks), so the
+// results equal the SB = 1 form's to the bit. Group statistics of a group
+// wider than QB would read columns past the block before the super-block's
+// errors reach them, so such groups take SB = 1.
+template <typename WT, bool WHOLE, int RG, int XW, int LZ = 0, int SB = 1>
 __global__ void __launch_bounds__(QT * RG * XW, RG * XW == 1 && LZ == 0 ? 2 : 1)
 gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __restrict__ U, int d_row, int d_col,
            int bits, int sym, int group, int ngroups, int vec4, uint8_t* __restrict__ codes, float* __restrict__ scales,
@@ -234,8 +280,9 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
            double* __restrict__ wg_loss, int lazyb) {
   static_assert(WHOLE || (RG == 1 && XW == 1), "the checked form takes one row group of 4 waves");
   static_assert(LZ == 0 || !WHOLE, "other lazy-batch widths take the checked form");
-  constexpr int NT = QT * RG * XW, NR = QR * RG;  // threads and rows per workgroup
-  constexpr int EW = LZ == 2 ? LZ_MAX_B : QB;     // error columns kept in LDS
+  static_assert(SB == 1 || (WHOLE && LZ == 0), "super-blocks only in the whole-tile form");
+  constexpr int NT = QT * RG * XW, NR = QR * RG;       // threads and rows per workgroup
+  constexpr int EW = LZ == 2 ? LZ_MAX_B : SB * QB;     // error columns kept in LDS
   __shared__ __attribute__((aligned(16))) float Ud[QB][QB];
   __shared__ float Es[NR][EW + 4];
   __shared__ uint8_t Cs[NR][QB];
@@ -275,7 +322,8 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
   for (int i1 = 0; i1 < d_col; i1 += QB) {
     const int nvalid = d_col - i1 < QB ? d_col - i1 : QB;
     const bool first = (i1 == 0);
-    const int kk0 = LZ == 2 ? i1 % lazyb : 0;  // this block's first error column in Es
+    // this block's first error column in Es
+    const int kk0 = LZ == 2 ? i1 % lazyb : SB > 1 ? i1 % (SB * QB) : 0;
 
     // 1. U block (upper part; padded columns act as identity rows) and W block.
     if (vec4 && nvalid == QB) {
@@ -405,8 +453,18 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
 
     // 4. Deferred update of the later columns: W[:, i2:] -= E U[blk, i2:].
     const int i2 = i1 + QB;
-    if constexpr (WHOLE) {
-      if (i2 < d_col) trailing_update_whole<WT, RG, XW>(W, Wf, U, Es, d_col, row0, i1, first);
+    if constexpr (WHOLE && SB == 1) {
+      if (i2 < d_col) trailing_update_whole<WT, RG, XW, EW + 4>(W, Wf, U, Es, d_col, row0, i2, d_col, i1, 0, 1, first);
+    } else if constexpr (WHOLE) {
+      // Inside a super-block, this block's errors go to the rest of the
+      // super-block; at its end, all of its errors go to the later columns.
+      const int o1 = i1 - kk0;
+      const int o2 = o1 + SB * QB < d_col ? o1 + SB * QB : d_col;
+      if (i2 < o2)
+        trailing_update_whole<WT, RG, XW, EW + 4>(W, Wf, U, Es, d_col, row0, i2, o2, i1, kk0, 1, first);
+      else if (o2 < d_col)
+        trailing_update_whole<WT, RG, XW, EW + 4>(W, Wf, U, Es, d_col, row0, o2, d_col, o1, 0, (o2 - o1) / QB,
+                                                  o1 == 0);
     } else if (LZ == 2) {
       // Inside a B-block, this block's errors go to the rest of the B-block;
       // at its end, all of the B-block's errors go to the later columns (a
@@ -667,16 +725,20 @@ int launch_quantize(const void* W, int wdtype, int64_t d_row, int64_t d_col, con
   // take 32 rows per workgroup, halving the U rows each row's update streams.
   // Lazy-batch widths above the block take the checked form with two-level
   // deferral; those that divide the block nest inside it (see gptq_sweep).
+  // The 32-row and 8-wave forms hold one workgroup per CU and defer in
+  // super-blocks of SUPER_BLOCKS blocks, which groups wider than the block
+  // do not allow; such layers take the 16-row form.
   const int lz = block > QB ? 2 : 0;
   const bool whole = lz == 0 && vec4 && d_col % 64 == 0 && d_row % QR == 0;
-  const int rg = (whole && d_row % (2 * QR) == 0 && d_row >= RG2_MIN_ROWS && d_col >= RG2_MIN_COLS) ? 2 : 1;
+  const bool super = whole && (group_size == -1 || group_size <= QB);
+  const int rg = (super && d_row % (2 * QR) == 0 && d_row >= RG2_MIN_ROWS && d_col >= RG2_MIN_COLS) ? 2 : 1;
   const unsigned nwg = unsigned((d_row + rg * QR - 1) / (rg * QR));
   // Layers small enough that every CU holds at most one 16-row workgroup
   // give it 8 waves: the extra 4 work only in the deferred update.
-  const int xw = (whole && rg == 1 && nwg <= XW2_MAX_WG) ? 2 : 1;
+  const int xw = (super && rg == 1 && nwg <= XW2_MAX_WG) ? 2 : 1;
   if (wdtype == GPTQ_F16) {
-    auto k = rg == 2 ? gptq_sweep<__half, true, 2, 1>
-             : xw == 2 ? gptq_sweep<__half, true, 1, 2>
+    auto k = rg == 2 ? gptq_sweep<__half, true, 2, 1, 0, SUPER_BLOCKS>
+             : xw == 2 ? gptq_sweep<__half, true, 1, 2, 0, SUPER_BLOCKS>
              : whole ? gptq_sweep<__half, true, 1, 1>
              : lz == 2 ? gptq_sweep<__half, false, 1, 1, 2>
                      : gptq_sweep<__half, false, 1, 1>;
@@ -684,8 +746,8 @@ int launch_quantize(const void* W, int wdtype, int64_t d_row, int64_t d_col, con
                        int(d_col), bits, symmetric, int(group_size), ngroups, vec4, codes, scales, zeros, packed, nwords,
                        row_loss, w.wg_loss, int(block));
   } else {
-    auto k = rg == 2 ? gptq_sweep<float, true, 2, 1>
-             : xw == 2 ? gptq_sweep<float, true, 1, 2>
+    auto k = rg == 2 ? gptq_sweep<float, true, 2, 1, 0, SUPER_BLOCKS>
+             : xw == 2 ? gptq_sweep<float, true, 1, 2, 0, SUPER_BLOCKS>
              : whole ? gptq_sweep<float, true, 1, 1>
              : lz == 2 ? gptq_sweep<float, false, 1, 1, 2>
                      : gptq_sweep<float, false, 1, 1>;

@@ -160,6 +160,46 @@ inline int __float_as_int(float f) {
   return v;
 }
 
+// Raw buffer resources: a base, a size in bytes and the 32-bit offsets of
+// each access. The kernels keep every access inside the size they give, so
+// an access past it (which the hardware would drop or read as zero) is
+// reported here as an error.
+struct __amdgpu_buffer_rsrc_t {
+  char* base;
+  uint32_t bytes;
+};
+namespace simt {
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+inline char* buffer_at(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t n) {
+  const uint64_t off = uint64_t(voff) + uint64_t(soff);
+  if (off + n > r.bytes) {
+    std::fprintf(stderr, "host emulation: buffer access at byte %llu (+%u) past the resource's %u bytes\n",
+                 (unsigned long long)off, n, r.bytes);
+    std::abort();
+  }
+  return r.base + off;
+}
+template <typename V>
+inline V buffer_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  V v;
+  std::memcpy(&v, buffer_at(r, voff, soff, sizeof(V)), sizeof(V));
+  return v;
+}
+}  // namespace simt
+inline __amdgpu_buffer_rsrc_t __builtin_amdgcn_make_buffer_rsrc(void* base, short stride, int bytes, int flags) {
+  if (stride != 0) std::abort();
+  (void)flags;
+  return __amdgpu_buffer_rsrc_t{static_cast<char*>(base), uint32_t(bytes)};
+}
+#define __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, aux) simt::buffer_load<simt::u32x4_t>((r), (voff), (soff))
+#define __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, aux) simt::buffer_load<simt::u32x2_t>((r), (voff), (soff))
+#define __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, aux) \
+  do {                                                                \
+    const simt::u32x4_t v_ = (v);                                     \
+    std::memcpy(simt::buffer_at((r), (voff), (soff), 16), &v_, 16);   \
+  } while (0)
+
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) simt::dpp((src), (ctrl), (rm), (bm))
 #define __builtin_amdgcn_mov_dpp(src, ctrl, rm, bm, bc) simt::dpp((src), (ctrl), (rm), (bm))
 #define __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, cbsz, abid, blgp) simt::mfma_16x16x4f32((a), (b), (c))

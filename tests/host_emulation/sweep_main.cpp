@@ -52,7 +52,9 @@ int direct(int rg, int xw, const void* W, int64_t d_row, int64_t d_col, const fl
   const int ngroups = group == -1 ? 1 : int((d_col + group - 1) / group);
   const int nwords = int((d_col * bits + 31) / 32);
   const unsigned nwg = unsigned(d_row / (rg * QR));
-  auto k = rg == 2 ? gptq_sweep<WT, true, 2, 1> : xw == 2 ? gptq_sweep<WT, true, 1, 2> : gptq_sweep<WT, true, 1, 1>;
+  auto k = rg == 2   ? gptq_sweep<WT, true, 2, 1, 0, SUPER_BLOCKS>
+           : xw == 2 ? gptq_sweep<WT, true, 1, 2, 0, SUPER_BLOCKS>
+                     : gptq_sweep<WT, true, 1, 1>;
   hipLaunchKernelGGL(k, dim3(nwg), dim3(rg * xw * QT), 0, nullptr, static_cast<const WT*>(W), w.Wf, U, int(d_row),
                      int(d_col), bits, 0, int(group), ngroups, 1, codes, scales, zeros, packed, nwords, row_loss,
                      w.wg_loss, 128);
@@ -99,12 +101,16 @@ int main(int argc, char** argv) {
 
   const std::string m = mode;
   int st;
+  // Workspace and scratch start as NaN (all bits set): a read of an element
+  // the kernels did not write first shows up in the outputs.
   if (m == "noalloc") {
+    std::memset(gptq::scratch, 0xFF, sizeof(gptq::scratch));
     st = gptq_quantize_layer_noalloc(W, wdtype, d_row, d_col, U, bits, group, block, sym, codes, scales, zeros, packed,
                                      loss, row_loss, nullptr);
   } else {
     const size_t wsb = gptq_quantize_layer_workspace_size(d_row, d_col, bits, group, block);
     void* ws = exact(wsb);
+    std::memset(ws, 0xFF, wsb);
     if (m == "ws")
       st = gptq_quantize_layer(W, wdtype, d_row, d_col, U, bits, group, block, sym, codes, scales, zeros, packed, loss,
                                row_loss, ws, wsb, nullptr);

@@ -439,14 +439,29 @@ def test_identity_hessian_symmetric_is_rtn_bit_exact(gpu, bits, group):
     assert np.allclose(q.scales.cpu().numpy(), ref["scales"], rtol=1e-7)
 
 
-def test_quantize_is_deterministic(gpu):
-    U = gpu_tensor(oracle_u(384, 3))
-    W = gpu_tensor((0.02 * np.random.default_rng(9).standard_normal((80, 384))).astype(np.float16))
-    a = gpu.gptq_quantize_layer(W, U, 4, 128)
-    b = gpu.gptq_quantize_layer(W, U, 4, 128)
+@pytest.mark.parametrize("d_row,d_col,bits,group,wdt", [
+    (80, 384, 4, 128, np.float16),  # 8 waves, one partial super-block
+    (64, 2048, 3, 128, np.float16),  # 8 waves, four 512-column super-blocks
+    (4112, 1280, 4, -1, np.float32),  # 16 rows per workgroup, 257 workgroups
+    (31, 260, 4, 256, np.float32),  # the checked form
+    (16384, 12288, 3, 128, np.float16),  # 32 rows per workgroup, super-blocks
+])
+def test_quantize_is_deterministic(gpu, d_row, d_col, bits, group, wdt):
+    """Three calls, each with a fresh workspace (whose memory may still hold
+    an earlier call's working copy), give the same bits. U is any
+    upper-triangular factor with a positive diagonal."""
+    say("determinism", d_row, d_col, bits, group, wdt.__name__)
+    r = np.random.default_rng(d_row + d_col)
+    U = np.triu(r.standard_normal((d_col, d_col), dtype=np.float32)) * np.float32(0.3 / np.sqrt(d_col))
+    U[np.diag_indices(d_col)] = 1.0
+    Ud = gpu_tensor(U)
+    Wd = gpu_tensor((0.02 * r.standard_normal((d_row, d_col), dtype=np.float32)).astype(wdt))
+    del U
+    qs = [gpu.gptq_quantize_layer(Wd, Ud, bits, group, 128) for _ in range(3)]
     torch.cuda.synchronize()
-    for x, y in [(a.codes, b.codes), (a.scales, b.scales), (a.packed, b.packed), (a.loss, b.loss)]:
-        assert torch.equal(x, y)
+    for q in qs[1:]:
+        for name in ("codes", "scales", "zeros", "packed", "row_loss", "loss"):
+            assert torch.equal(getattr(q, name), getattr(qs[0], name)), name
 
 
 # -------------------------------------------------------------------- pack
@@ -454,9 +469,11 @@ def test_quantize_is_deterministic(gpu):
                                             (np.float16, 3, 512), (np.float16, 4, 384)])
 def test_tall_layer_row_groups_are_bit_identical(gpu, wdt, bits, group):
     """Tile-aligned layers with at least 16384 rows (a multiple of 32) and
-    12288 columns take 32 rows per workgroup, others 16. A row's MFMA
-    sequence is the same either way, so the 16384-row layer and the same
-    layer one 16-row group shorter agree bit for bit on the rows both have;
+    12288 columns take 32 rows per workgroup and 512-column super-blocks
+    (groups of at most 128 columns), others 16 rows and no super-blocks. A
+    row element's fp32 MFMA sequence is the same either way, so the
+    16384-row layer and the same layer one 16-row group shorter agree bit
+    for bit on the rows both have;
     the tall one also matches the oracle on sampled rows. Groups wider than
     a block (256, 384, 512) read columns past the block for their
     statistics. U is any upper-triangular factor with a positive diagonal
@@ -479,9 +496,11 @@ def test_tall_layer_row_groups_are_bit_identical(gpu, wdt, bits, group):
 @pytest.mark.parametrize("wdt,bits,group", [(np.float16, 4, 128), (np.float32, 3, -1)])
 def test_small_layer_update_waves_are_bit_identical(gpu, wdt, bits, group):
     """Tile-aligned layers of at most 256 workgroups (4096 rows) run 8 waves
-    per workgroup, the extra 4 only in the deferred update; with one more
-    16-row group the layer runs 4. The shared rows agree bit for bit."""
-    d_col = 512
+    per workgroup, the extra 4 only in the deferred update, and defer the
+    update of columns past a 512-column super-block to its end; with one
+    more 16-row group the layer runs 4 waves and updates after every block.
+    The shared rows agree bit for bit."""
+    d_col = 1280  # two 512-column super-blocks and a half one in the 8-wave form
     U = oracle_u(d_col, 96)
     W = (0.02 * np.random.default_rng(95).standard_normal((4112, d_col))).astype(wdt)
     Ud, Wd = gpu_tensor(U), gpu_tensor(W)

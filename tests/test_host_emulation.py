@@ -16,8 +16,10 @@ and one-row layers, row counts that leave a workgroup partly empty, column
 counts with a partial last block and a partial last 64-column chunk,
 unaligned weights, groups wider than the block, lazy-batch widths below and
 above the block, the symmetric grid, the allocation-free entry point, and
-the whole-tile, 32-row and 8-wave instantiations. The outputs must also pass
-the same oracle parity check as the GPU tests.
+the whole-tile, 32-row and 8-wave instantiations, the last two over several
+512-column super-blocks. The outputs must also pass the same oracle parity
+check as the GPU tests, and the super-block forms must give the 16-row
+form's outputs to the bit.
 """
 
 from __future__ import annotations
@@ -110,7 +112,14 @@ CASES = [
     (64, 256, 4, 128, np.float16, {"mode": "w1"}),
     (64, 512, 3, -1, np.float32, {"mode": "rg2"}),
     (32, 384, 2, 64, np.float16, {"mode": "xw2"}),
+    # super-blocks of 512 columns: two whole ones and a half one
+    (64, 1280, 3, -1, np.float16, {"mode": "rg2"}),
+    (64, 1280, 3, -1, np.float16, {"mode": "w1"}),
+    (32, 1152, 2, 64, np.float32, {"mode": "xw2"}),
+    (32, 1152, 2, 64, np.float32, {"mode": "w1"}),
 ]
+# (form, form) pairs on the same inputs whose outputs must agree to the bit
+SAME = [((64, 1280, 3, -1, np.float16), "rg2", "w1"), ((32, 1152, 2, 64, np.float32), "xw2", "w1")]
 
 
 def test_sweep_source_runs_in_bounds_under_sanitizers(sweep_host):
@@ -134,4 +143,10 @@ def test_sweep_source_runs_in_bounds_under_sanitizers(sweep_host):
         check_quant(out, ref, bits, rerun_for(W, U, bits, group, block, symmetric=sym), label=str(case), log=None)
         loss = float(rd("loss", np.float64, (1,))[0])
         assert loss == pytest.approx(float(out.row_loss.astype(np.float64).sum()), rel=1e-6)
+    dirs = {(c[:5], c[5].get("mode", "ws")): d for c, d, *_ in results}
+    for shape, a, b in SAME:
+        for name in ("codes", "scales", "zeros", "packed", "row_loss"):
+            with open(os.path.join(dirs[(shape, a)], name + ".bin"), "rb") as fa, \
+                    open(os.path.join(dirs[(shape, b)], name + ".bin"), "rb") as fb:
+                assert fa.read() == fb.read(), f"{shape}: {name} of {a} and {b} differ"
     shutil.rmtree(str(work), ignore_errors=True)
