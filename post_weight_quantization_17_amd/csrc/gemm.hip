@@ -9,20 +9,22 @@
 //
 // Design (gfx950), one workgroup of 8 waves (two per SIMD) per 256-token x
 // 128-weight-row output tile, K (d_in) in tiles of 64:
-//  * X tiles [256 tokens][64] fp16 go through registers into LDS (row pitch
-//    72 halfs, so the 16-byte fragment reads of 32 consecutive rows fall on
-//    distinct banks).
-//  * d_in must be a multiple of 32; a last K tile of 32 columns is padded
-//    with zeros in LDS (nothing past d_in is read).
-//  * W tiles are cut from the packed words: each thread takes one 32-code
-//    unit (bits words of one row hold exactly 32 codes) per K tile, forms
-//    s (c - z) in fp32, rounds it to fp16 and stores the 32 halfs into the
-//    LDS tile [128 rows][64] (same pitch).
-//  * Each wave computes 128 tokens x 64 rows with v_mfma_f32_32x32x16_f16
-//    (4 x 2 tiles): A fragments are 8 consecutive K of one token, B
+//  * X tiles [256 tokens][64] fp16 move straight from HBM into LDS
+//    (global_load_lds, 16 bytes per lane) in three stages, the tile for
+//    K step kt + 2 in flight while step kt runs; 16-byte chunk c of row r
+//    sits at slot c ^ (r & 7), so the fragment reads of 32 consecutive rows
+//    fall on distinct banks.
+//  * d_in must be a multiple of 32; in a last K tile of 32 columns the
+//    chunks past d_in re-read chunks 0-3 of the same tile, and the weights
+//    they meet are zero (nothing past d_in is read).
+//  * W tiles are cut from the packed words: the 256 units of a K tile (128
+//    rows x 2 units of 32 codes; bits words of one row hold exactly 32
+//    codes) are split in halves of 16 codes over waves 0-3 and 4-7; each
+//    forms s (c - z) in fp32, rounds it to fp16 and stores the halfs into
+//    the LDS tile [128 rows][64] (row pitch 72 halfs), double-buffered.
+//  * Each wave computes 64 tokens x 64 rows with v_mfma_f32_32x32x16_f16
+//    (2 x 2 tiles): A fragments are 8 consecutive K of one token, B
 //    fragments 8 consecutive K of one weight row, both 16-byte LDS reads.
-//  * Two LDS stages: the next K tile's global loads are issued before the
-//    current tile's MFMAs and its dequantization runs beside them.
 //  * Epilogue: optional ReLU on the fp32 sum, then round to fp16.
 // fp16 x fp16 products are exact in fp32; the sums are fp32 (MFMA order).
 #include "gptq_common.h"

@@ -48,9 +48,6 @@ constexpr int QM = QB / 16;    // columns per lane per block
 // there are enough rows for full rounds of one-per-CU workgroups.
 constexpr int RG2_MIN_ROWS = 16384;
 constexpr int RG2_MIN_COLS = 12288;
-// Whole-tile layers of at most this many 16-row workgroups (one per CU)
-// take 8 waves per workgroup.
-constexpr int XW2_MAX_WG = 256;
 // Largest lazy-batch width (a multiple of QB) the sweep takes.
 constexpr int LZ_MAX_B = 1024;
 // Blocks per super-block of the 32-row and 8-wave whole-tile forms.
@@ -727,15 +724,19 @@ int launch_quantize(const void* W, int wdtype, int64_t d_row, int64_t d_col, con
   // deferral; those that divide the block nest inside it (see gptq_sweep).
   // The 32-row and 8-wave forms hold one workgroup per CU and defer in
   // super-blocks of SUPER_BLOCKS blocks, which groups wider than the block
-  // do not allow; such layers take the 16-row form.
+  // do not allow; such layers take the 4-wave 16-row form (two workgroups
+  // per CU).
   const int lz = block > QB ? 2 : 0;
   const bool whole = lz == 0 && vec4 && d_col % 64 == 0 && d_row % QR == 0;
   const bool super = whole && (group_size == -1 || group_size <= QB);
   const int rg = (super && d_row % (2 * QR) == 0 && d_row >= RG2_MIN_ROWS && d_col >= RG2_MIN_COLS) ? 2 : 1;
   const unsigned nwg = unsigned((d_row + rg * QR - 1) / (rg * QR));
-  // Layers small enough that every CU holds at most one 16-row workgroup
-  // give it 8 waves: the extra 4 work only in the deferred update.
-  const int xw = (super && rg == 1 && nwg <= XW2_MAX_WG) ? 2 : 1;
+  // The other super-block layers take 16 rows and 8 waves per workgroup
+  // (one workgroup per CU): the extra 4 waves work only in the deferred
+  // update. Measured against two 4-wave workgroups per CU without
+  // super-blocks: 12288 x 12288, 19.3 against 28.9 ms; 11008 x 4096, 2.84
+  // against 2.90 ms.
+  const int xw = (super && rg == 1) ? 2 : 1;
   if (wdtype == GPTQ_F16) {
     auto k = rg == 2 ? gptq_sweep<__half, true, 2, 1, 0, SUPER_BLOCKS>
              : xw == 2 ? gptq_sweep<__half, true, 1, 2, 0, SUPER_BLOCKS>

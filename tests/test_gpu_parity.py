@@ -442,7 +442,7 @@ def test_identity_hessian_symmetric_is_rtn_bit_exact(gpu, bits, group):
 @pytest.mark.parametrize("d_row,d_col,bits,group,wdt", [
     (80, 384, 4, 128, np.float16),  # 8 waves, one partial super-block
     (64, 2048, 3, 128, np.float16),  # 8 waves, four 512-column super-blocks
-    (4112, 1280, 4, -1, np.float32),  # 16 rows per workgroup, 257 workgroups
+    (4112, 1280, 4, 256, np.float32),  # 4-wave whole-tile form (groups wider than a block)
     (31, 260, 4, 256, np.float32),  # the checked form
     (16384, 12288, 3, 128, np.float16),  # 32 rows per workgroup, super-blocks
 ])
@@ -494,15 +494,16 @@ def test_tall_layer_row_groups_are_bit_identical(gpu, wdt, bits, group):
 
 
 @pytest.mark.parametrize("wdt,bits,group", [(np.float16, 4, 128), (np.float32, 3, -1)])
-def test_small_layer_update_waves_are_bit_identical(gpu, wdt, bits, group):
-    """Tile-aligned layers of at most 256 workgroups (4096 rows) run 8 waves
-    per workgroup, the extra 4 only in the deferred update, and defer the
-    update of columns past a 512-column super-block to its end; with one
-    more 16-row group the layer runs 4 waves and updates after every block.
-    The shared rows agree bit for bit."""
-    d_col = 1280  # two 512-column super-blocks and a half one in the 8-wave form
+def test_update_forms_are_bit_identical(gpu, wdt, bits, group):
+    """Tile-aligned layers (here 4096 rows) run 8 waves per 16-row workgroup,
+    the extra 4 only in the deferred update, and defer the update of columns
+    past a 512-column super-block to its end; one more row makes the layer
+    ragged, and it runs the checked 4-wave form, which updates after every
+    block. A row element's fp32 MFMA sequence is the same in both, so the
+    shared rows agree bit for bit."""
+    d_col = 1280  # two 512-column super-blocks and a half one
     U = oracle_u(d_col, 96)
-    W = (0.02 * np.random.default_rng(95).standard_normal((4112, d_col))).astype(wdt)
+    W = (0.02 * np.random.default_rng(95).standard_normal((4097, d_col))).astype(wdt)
     Ud, Wd = gpu_tensor(U), gpu_tensor(W)
     qa = gpu.gptq_quantize_layer(Wd[:4096].contiguous(), Ud, bits, group, 128)
     qb = gpu.gptq_quantize_layer(Wd, Ud, bits, group, 128)
