@@ -734,9 +734,9 @@ hinv_write_u(const double* __restrict__ R, int d, float* __restrict__ U) {
   }
 }
 
-// Panel buffers: super-panel p writes buffer p % NPANEL, which the trailing
-// updates of p and p + 1 read.
-constexpr int NPANEL = 3;
+// Panel buffers: super-panel p writes buffer p % NPANEL; the trailing
+// updates of p and p + 1 read it (see the schedule at gptq_prepare_hinv).
+constexpr int NPANEL = 5;
 
 struct HinvWs {
   double *A, *R, *LT, *lam;
@@ -747,12 +747,14 @@ HinvWs carve(void* ws, int64_t d) {
   HinvWs w{};
   const size_t mat = align_up(size_t(d) * d * sizeof(double), 256);
   const size_t panel = align_up(size_t(NPANEL) * KS * d * sizeof(double), 256);
-  char* p = static_cast<char*>(ws);
-  w.A = reinterpret_cast<double*>(p);
-  w.R = reinterpret_cast<double*>(p + mat);
-  w.LT = reinterpret_cast<double*>(p + 2 * mat);
-  w.lam = reinterpret_cast<double*>(p + 2 * mat + panel);
   w.bytes = 2 * mat + panel + 256;
+  if (ws != nullptr) {  // sizes only when there is no workspace yet
+    char* p = static_cast<char*>(ws);
+    w.A = reinterpret_cast<double*>(p);
+    w.R = reinterpret_cast<double*>(p + mat);
+    w.LT = reinterpret_cast<double*>(p + 2 * mat);
+    w.lam = reinterpret_cast<double*>(p + 2 * mat + panel);
+  }
   return w;
 }
 
@@ -761,7 +763,7 @@ HinvWs carve(void* ws, int64_t d) {
 // concurrent callers cannot interleave their event records.
 struct AuxCtx {
   hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, chain[NPANEL] = {}, trail[NPANEL] = {};
+  hipEvent_t fork = nullptr, join = nullptr, chain[NPANEL] = {}, strip2[NPANEL] = {}, strip3[NPANEL] = {};
   bool ready = false;
 };
 std::mutex g_aux_mu;
@@ -773,10 +775,11 @@ AuxCtx* aux_context() {
   AuxCtx& c = g_aux[dev];
   if (!c.ready) {
     if (hipStreamCreateWithFlags(&c.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    hipEvent_t* evs[2 + 2 * NPANEL] = {&c.fork, &c.join};
+    hipEvent_t* evs[2 + 3 * NPANEL] = {&c.fork, &c.join};
     for (int i = 0; i < NPANEL; ++i) {
       evs[2 + i] = &c.chain[i];
-      evs[2 + NPANEL + i] = &c.trail[i];
+      evs[2 + NPANEL + i] = &c.strip2[i];
+      evs[2 + 2 * NPANEL + i] = &c.strip3[i];
     }
     for (hipEvent_t* e : evs)
       if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return nullptr;
@@ -843,19 +846,31 @@ extern "C" size_t gptq_prepare_hinv_workspace_size(int64_t d) {
 }
 
 // Schedule (S = the caller's stream, X = the auxiliary stream). Strip q is
-// super-panel q's columns of A and its rows of R. For each super-panel
-// p = [s0, s1):
-//   S: the super-panel step of p (writing the panel buffer LT[p % 3])
-//   S: "trail A": apply p - 1 and p (K = 256; p alone for p = 0) to strip
-//      p + 1, after waiting for trail B of p - 2, the last other writer of
-//      that strip
-//   X: after trail A, "trail B": apply p to strips p + 3 and beyond,
-//      overlapping the next super-panel steps on S
-// Trail B of p - 1 stops short of strip p + 1, so trail A never waits for the
-// trail B just launched beside it: the one it waits for had two super-panel
-// steps to finish. The writers of each tile and panel buffer are ordered by
-// stream order or an event: trail A of p waits for trail B of p - 2, which is
-// also the last reader of the buffer that step p + 1 overwrites.
+// super-panel q's columns of A (all rows below) and its rows of R. For each
+// super-panel p = [s0, s1):
+//   S: the super-panel step of p (writing the panel buffer LT[p % 5])
+//   S: "trail A": the super-panels that strip p + 1 still lacks, applied to it
+//   X: after trail A, the rest of the trailing update, overlapping the next
+//      super-panel steps on S
+// Below PAIR_MIN_D ("single" form): trail A applies p - 1 and p (K = 256;
+// p alone for p = 0), and X applies p alone to strips p + 3 and beyond. Trail
+// A of p waits for X's work of p - 2, the last other writer of strip p + 1.
+// From PAIR_MIN_D on ("paired" form), X works only at odd p and applies p - 1
+// and p together (K = 256): to strip p + 2, then strip p + 3, then strips
+// p + 4 and beyond (the bulk). Each element of the trailing matrices is then
+// read and written once per two super-panels. Trail A applies p - 1 and p
+// for odd p and p alone for even p. It waits for X's strip-(p + 1) update
+// of p - 1 (event strip2) for even p, and of p - 2 (event strip3) for odd p.
+// In both forms X runs in order, so each wait also covers every X kernel
+// enqueued before the one waited for. That includes the last other writers
+// of strip p + 1 and the last readers of the panel buffer that step p + 1
+// overwrites (buffer (p - 4) % 5). Every strip receives every earlier
+// super-panel exactly once before its step. U is the same to the bit in
+// both forms: each element sees the same fp64 MFMA sequence.
+// Measured (factor alone): d = 12288, 32.3 ms single, 30.7 ms paired;
+// d = 4096, 2.33 ms single, 2.43 ms paired (three X launches per two
+// super-panels instead of two).
+constexpr int PAIR_MIN_D = 8192;
 extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* lambda_out, int32_t* info,
                                  void* ws, size_t ws_bytes, void* stream) {
   if (d < 1 || d > 65536 || H == nullptr || U == nullptr || info == nullptr) return GPTQ_E_INVALID_ARG;
@@ -869,8 +884,8 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
 
   hipStream_t x = ctx ? ctx->aux : s;
   // Under stream capture the events are recorded by hipEventRecord, whose
-  // capture semantics are the documented ones; otherwise trail A's launch
-  // records its event itself.
+  // capture semantics are the documented ones; otherwise the launches of
+  // trail A and of X's strip updates record their events themselves.
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cap) != hipSuccess) return GPTQ_E_HIP;
   const bool by_launch = ctx && cap == hipStreamCaptureStatusNone;
@@ -886,8 +901,16 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(x, ctx->fork, 0) != hipSuccess)
       return GPTQ_E_HIP;
   }
+  auto bound = [&](int a) { return a < di ? a : di; };
+  const bool paired = di >= PAIR_MIN_D;
+  // a strip update of X, recording `ev` (by the launch when possible)
+  auto strip_update = [&](const double* LT0, const double* LT, TrailSpec sp, hipEvent_t ev) -> bool {
+    if (!launch_trail(x, w, LT0, LT, di, sp, false, by_launch ? ev : nullptr)) return false;
+    if (launch_status() != GPTQ_OK) return false;
+    return !ctx || by_launch || hipEventRecord(ev, x) == hipSuccess;
+  };
   for (int p = 0, s0 = 0; s0 < di; ++p, s0 += KS) {
-    const int s1 = di - s0 < KS ? di : s0 + KS;
+    const int s1 = bound(s0 + KS);
     double* LTw = w.LT + size_t(p % NPANEL) * KS * di;
     const int kb0 = s1 - s0 < NB ? s1 - s0 : NB;
     const int kb1 = s1 - s0 - kb0;
@@ -898,24 +921,38 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     const StepArgs args{w.A, w.R, LTw, di, s0, kb0, kb1, nrow, ncol, ntile};
     hipLaunchKernelGGL(hinv_step, dim3(unsigned(grid)), dim3(256), 0, s, args, info);
     if (s1 < di) {
-      const int s2 = di - s1 < KS ? di : s1 + KS;
-      const int s3 = di - s2 < KS ? di : s2 + KS;
-      if (ctx && p >= 2 && hipStreamWaitEvent(s, ctx->trail[(p - 2) % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
-      // trail A: columns [s1, s2) of A (all rows below), rows [s1, s2) of R,
-      // from super-panels p - 1 (whose trail B left them out) and p
-      const int p0 = p >= 1 ? s0 - KS : s0;
-      const double* LT0 = p >= 1 ? w.LT + size_t((p - 1) % NPANEL) * KS * di : LTw;
+      const int s2 = bound(s1 + KS), s3 = bound(s2 + KS), s4 = bound(s3 + KS);
+      const bool odd = (p & 1) != 0;
+      const bool two = paired ? odd : p >= 1;  // trail A applies p - 1 too
+      if (ctx && p >= 2) {
+        hipEvent_t ev = (!paired || odd) ? ctx->strip3[(p - 2) % NPANEL] : ctx->strip2[(p - 1) % NPANEL];
+        if (hipStreamWaitEvent(s, ev, 0) != hipSuccess) return GPTQ_E_HIP;
+      }
+      // trail A: columns [s1, s2) of A (all rows below), rows [s1, s2) of R
+      const int p0 = two ? s0 - KS : s0;
+      const double* LT0 = two ? w.LT + size_t((p - 1) % NPANEL) * KS * di : LTw;
       if (!launch_trail(s, w, LT0, LTw, di, TrailSpec{s0, s1, s1, 0, s1, s2 - s1, s1, s2 - s1, p0}, false,
                         by_launch ? ctx->chain[p % NPANEL] : nullptr))
         return GPTQ_E_HIP;
       if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
       if (ctx && !by_launch && hipEventRecord(ctx->chain[p % NPANEL], s) != hipSuccess) return GPTQ_E_HIP;
-      // trail B: A at and beyond s3 (lower triangle), R rows from s3. It
-      // starts once trail A is done, so that trail A (on the critical path)
-      // has the GPU to itself and trail B overlaps the next panel steps.
-      if (ctx && hipStreamWaitEvent(x, ctx->chain[p % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
-      if (s3 < di) launch_trail(x, w, LTw, LTw, di, TrailSpec{s0, s1, s3, 0, 0, 0, s3, di - s3, s0}, true);
-      if (ctx && hipEventRecord(ctx->trail[p % NPANEL], x) != hipSuccess) return GPTQ_E_HIP;
+      if (!paired) {
+        // X: p applied to strips p + 3 and beyond (A at and beyond s3, lower
+        // triangle; R rows from s3), after trail A
+        if (ctx && hipStreamWaitEvent(x, ctx->chain[p % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
+        if (s3 < di) launch_trail(x, w, LTw, LTw, di, TrailSpec{s0, s1, s3, 0, 0, 0, s3, di - s3, s0}, true);
+        if (ctx && hipEventRecord(ctx->strip3[p % NPANEL], x) != hipSuccess) return GPTQ_E_HIP;
+      } else if (odd && s2 < di) {
+        // X: p - 1 and p applied to strip p + 2, strip p + 3, then the rest
+        // (A at and beyond s4, lower triangle; R rows from s4). It starts
+        // once trail A is done, so that trail A (on the critical path) has
+        // the GPU to itself, and overlaps the next super-panel steps.
+        if (ctx && hipStreamWaitEvent(x, ctx->chain[p % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
+        hipEvent_t e2 = ctx ? ctx->strip2[p % NPANEL] : nullptr, e3 = ctx ? ctx->strip3[p % NPANEL] : nullptr;
+        if (!strip_update(LT0, LTw, TrailSpec{s0, s1, s2, 0, s2, s3 - s2, s2, s3 - s2, p0}, e2)) return GPTQ_E_HIP;
+        if (!strip_update(LT0, LTw, TrailSpec{s0, s1, s3, 0, s3, s4 - s3, s3, s4 - s3, p0}, e3)) return GPTQ_E_HIP;
+        if (s4 < di) launch_trail(x, w, LT0, LTw, di, TrailSpec{s0, s1, s4, 0, 0, 0, s4, di - s4, p0}, true);
+      }
     }
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }

@@ -1,5 +1,6 @@
-"""The library's column-sweep source run on the CPU with AddressSanitizer and
-UndefinedBehaviorSanitizer (no GPU needed).
+"""The library's sources run on the CPU (no GPU needed): the column sweep
+under AddressSanitizer and UndefinedBehaviorSanitizer, and the factor's
+two-stream schedule.
 
 tests/host_emulation/ compiles post_weight_quantization_17_amd/csrc/quantize.hip
 for the host against small stand-ins for the HIP runtime: each workgroup runs
@@ -150,3 +151,32 @@ def test_sweep_source_runs_in_bounds_under_sanitizers(sweep_host):
                     open(os.path.join(dirs[(shape, b)], name + ".bin"), "rb") as fb:
                 assert fa.read() == fb.read(), f"{shape}: {name} of {a} and {b} differ"
     shutil.rmtree(str(work), ignore_errors=True)
+
+
+SCHED_FLAGS = ["-std=c++20", "-O0", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-pthread"]
+
+
+def test_factor_schedule_orders_every_strip_and_panel_buffer(tmp_path):
+    """tests/host_emulation/hinv_schedule.cpp compiles the factor's source
+    against record-only HIP stand-ins, replays the launches, event records
+    and stream waits of gptq_prepare_hinv, and checks on the log (with the
+    events recorded by the launches and, as under graph capture, by
+    hipEventRecord): launches that touch the same strip are ordered; each
+    trailing update reads a panel buffer after the step that wrote its panel
+    and before the step that overwrites it; every strip receives every
+    earlier super-panel exactly once before its own step. Sizes cover one
+    block, a partial super-panel, the remainders modulo 128 around block
+    edges, both schedule forms (single below 8192, paired from 8192 on) and
+    up to 96 super-panels."""
+    if not os.path.exists(CLANG):
+        pytest.skip("ROCm's clang++ is not installed")
+    exe = str(tmp_path / "hinv_schedule")
+    r = subprocess.run([CLANG, *SCHED_FLAGS, "-I", os.path.join(HERE, "record"), os.path.join(HERE, "hinv_schedule.cpp"),
+                        "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-4000:]
+    sizes = [1, 63, 64, 65, 127, 128, 129, 200, 255, 256, 257, 300, 383, 384, 385, 511, 512, 513, 640, 700, 1000,
+             1024, 1025, 2048, 3000, 4096, 5000, 8191, 8192, 8193, 11008, 12288]
+    p = subprocess.run([exe, *map(str, sizes)], capture_output=True, text=True, timeout=600)
+    assert p.returncode == 0, p.stderr[-4000:]
+    assert f"passed: {2 * len(sizes)}" in p.stdout
+
