@@ -14,13 +14,13 @@
  *     allocated (for instance with torch). The library never allocates,
  *     frees or retains caller memory.
  *   - Process-wide state (created on first use, kept until the process
- *     ends, never freed): gptq_prepare_hinv keeps, per device, one
- *     auxiliary stream (default priority) and a small set of events for its
+ *     ends, never freed): gptq_prepare_hinv keeps, per device, two
+ *     auxiliary streams (default priority) and a small set of events for its
  *     look-ahead, and serializes its own enqueueing with a host mutex, so
- *     concurrent factor calls on different streams share that auxiliary
- *     stream and their device work overlaps less; while a caller captures a
+ *     concurrent factor calls on different streams share those auxiliary
+ *     streams and their device work overlaps less; while a caller captures a
  *     factor call into a graph, no other thread may call gptq_prepare_hinv
- *     on that device (the shared auxiliary stream is then part of the
+ *     on that device (the shared auxiliary streams are then part of the
  *     capture). gptq_quantize_layer_noalloc uses one static scratch array
  *     per device (see there). The packed product caches the occupancy per
  *     kernel, taken on the first device it runs on. Nothing else is kept
@@ -114,8 +114,8 @@ int gptq_hessian_accumulate(const void* X, int xdtype, int64_t n_tokens, int64_t
  *              numerically positive definite, k - 1 being the column (in H's
  *              indexing) where the factorization broke down. U is then
  *              unspecified.
- * The factorization runs in fp64 on the device. Part of its work runs on a
- * per-device auxiliary stream that is forked from and joined back to
+ * The factorization runs in fp64 on the device. Part of its work runs on
+ * per-device auxiliary streams that are forked from and joined back to
  * `stream` by events within the call, so the call keeps the usual stream
  * semantics and can be captured into a HIP graph. Errors: d < 1, NULL H, U
  * or info, damp < 0 or not finite -> GPTQ_E_INVALID_ARG.

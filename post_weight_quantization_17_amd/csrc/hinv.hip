@@ -736,7 +736,7 @@ hinv_write_u(const double* __restrict__ R, int d, float* __restrict__ U) {
 
 // Panel buffers: super-panel p writes buffer p % NPANEL; the trailing
 // updates of p and p + 1 read it (see the schedule at gptq_prepare_hinv).
-constexpr int NPANEL = 5;
+constexpr int NPANEL = 7;
 
 struct HinvWs {
   double *A, *R, *LT, *lam;
@@ -758,12 +758,13 @@ HinvWs carve(void* ws, int64_t d) {
   return w;
 }
 
-// Per-device auxiliary stream and events for the look-ahead (created once,
+// Per-device auxiliary streams and events for the look-ahead (created once,
 // kept until the process ends). Enqueueing a factorization holds a lock, so
 // concurrent callers cannot interleave their event records.
 struct AuxCtx {
-  hipStream_t aux = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr, chain[NPANEL] = {}, strip2[NPANEL] = {}, strip3[NPANEL] = {};
+  hipStream_t aux = nullptr, aux2 = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, join2 = nullptr, chain[NPANEL] = {}, strip2[NPANEL] = {},
+             strip3[NPANEL] = {}, bulk[NPANEL] = {};
   bool ready = false;
 };
 std::mutex g_aux_mu;
@@ -775,11 +776,13 @@ AuxCtx* aux_context() {
   AuxCtx& c = g_aux[dev];
   if (!c.ready) {
     if (hipStreamCreateWithFlags(&c.aux, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    hipEvent_t* evs[2 + 3 * NPANEL] = {&c.fork, &c.join};
+    if (hipStreamCreateWithFlags(&c.aux2, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    hipEvent_t* evs[3 + 4 * NPANEL] = {&c.fork, &c.join, &c.join2};
     for (int i = 0; i < NPANEL; ++i) {
-      evs[2 + i] = &c.chain[i];
-      evs[2 + NPANEL + i] = &c.strip2[i];
-      evs[2 + 2 * NPANEL + i] = &c.strip3[i];
+      evs[3 + i] = &c.chain[i];
+      evs[3 + NPANEL + i] = &c.strip2[i];
+      evs[3 + 2 * NPANEL + i] = &c.strip3[i];
+      evs[3 + 3 * NPANEL + i] = &c.bulk[i];
     }
     for (hipEvent_t* e : evs)
       if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return nullptr;
@@ -789,7 +792,13 @@ AuxCtx* aux_context() {
 }
 
 // bulk: the update beyond the next super-panel (throughput-bound: 128x128
-// tiles while there are at least 4 per CU, 64x64 below that; 16 k per chunk).
+// tiles while there are at least 4 per CU, 64x64 below that). The 128x128
+// form moves 8 k per chunk: its LDS (17 KB) and registers (208) then leave
+// room on a CU holding one of its workgroups for a super-panel step (136 KB,
+// 288 registers) or a look-ahead workgroup, so the critical chain runs beside
+// the bulk update instead of waiting for it to drain (with 16 k per chunk,
+// 34 KB, the step fitted on no CU the bulk update occupied). d = 12288:
+// factor 30.6 -> 29.0 ms.
 // look-ahead: the next super-panel's strip (K = 256), on the critical path
 // and bound by the latency of its dependent chunk loads: 32 k per chunk, and
 // 32x32 tiles while 64x64 ones would not give every CU one. A non-null
@@ -826,13 +835,17 @@ bool launch_trail(hipStream_t st, const HinvWs& w, const double* LT0, const doub
   }
   const int64_t n128 = tiles(128, q);
   if (n128 >= 4 * 256) {
-    hipLaunchKernelGGL((hinv_trail<128, 16>), dim3(unsigned(n128)), dim3(256), 0, st, w.A, w.R, LT0, LT, d, q);
-  } else {
-    const int64_t n64 = tiles(64, q);
-    if (n64 > 0)
-      hipLaunchKernelGGL((hinv_trail<64, 16>), dim3(unsigned(n64)), dim3(256), 0, st, w.A, w.R, LT0, LT, d, q);
+    hipExtLaunchKernelGGL((hinv_trail<128, 8>), dim3(unsigned(n128)), dim3(256), 0, st, nullptr, done, 0, w.A, w.R,
+                          static_cast<const double*>(LT0), static_cast<const double*>(LT), d, q);
+    return true;
   }
-  return true;
+  const int64_t n64 = tiles(64, q);
+  if (n64 > 0) {
+    hipExtLaunchKernelGGL((hinv_trail<64, 16>), dim3(unsigned(n64)), dim3(256), 0, st, nullptr, done, 0, w.A, w.R,
+                          static_cast<const double*>(LT0), static_cast<const double*>(LT), d, q);
+    return true;
+  }
+  return done == nullptr || hipEventRecord(done, st) == hipSuccess;
 }
 
 }  // namespace
@@ -845,31 +858,43 @@ extern "C" size_t gptq_prepare_hinv_workspace_size(int64_t d) {
   return carve(nullptr, d).bytes;
 }
 
-// Schedule (S = the caller's stream, X = the auxiliary stream). Strip q is
-// super-panel q's columns of A (all rows below) and its rows of R. For each
-// super-panel p = [s0, s1):
-//   S: the super-panel step of p (writing the panel buffer LT[p % 5])
+// Schedule (S = the caller's stream, X and Y = the auxiliary streams).
+// Strip q is super-panel q's columns of A (all rows below) and its rows of
+// R. For each super-panel p = [s0, s1):
+//   S: the super-panel step of p (writing the panel buffer LT[p % NPANEL])
 //   S: "trail A": the super-panels that strip p + 1 still lacks, applied to it
-//   X: after trail A, the rest of the trailing update, overlapping the next
-//      super-panel steps on S
-// Below PAIR_MIN_D ("single" form): trail A applies p - 1 and p (K = 256;
-// p alone for p = 0), and X applies p alone to strips p + 3 and beyond. Trail
-// A of p waits for X's work of p - 2, the last other writer of strip p + 1.
-// From PAIR_MIN_D on ("paired" form), X works only at odd p and applies p - 1
-// and p together (K = 256): to strip p + 2, then strip p + 3, then strips
-// p + 4 and beyond (the bulk). Each element of the trailing matrices is then
-// read and written once per two super-panels. Trail A applies p - 1 and p
-// for odd p and p alone for even p. It waits for X's strip-(p + 1) update
-// of p - 1 (event strip2) for even p, and of p - 2 (event strip3) for odd p.
-// In both forms X runs in order, so each wait also covers every X kernel
-// enqueued before the one waited for. That includes the last other writers
-// of strip p + 1 and the last readers of the panel buffer that step p + 1
-// overwrites (buffer (p - 4) % 5). Every strip receives every earlier
-// super-panel exactly once before its step. U is the same to the bit in
-// both forms: each element sees the same fp64 MFMA sequence.
-// Measured (factor alone): d = 12288, 32.3 ms single, 30.7 ms paired;
-// d = 4096, 2.33 ms single, 2.43 ms paired (three X launches per two
-// super-panels instead of two).
+//   X (and Y): after trail A, the rest of the trailing update, overlapping
+//      the next super-panel steps on S
+// Below PAIR_MIN_D ("single" form, X only): trail A applies p - 1 and p
+// (K = 256; p alone for p = 0), and X applies p alone to strips p + 3 and
+// beyond. Trail A of p waits for X's work of p - 2, the last other writer of
+// strip p + 1.
+// From PAIR_MIN_D on ("paired" form), the auxiliary streams work only at odd
+// p and apply p - 1 and p together (K = 256), so each element of the
+// trailing matrices is read and written once per two super-panels:
+//   Y: strip p + 2 (event strip2), strip p + 3 (event strip3), then, once X
+//      has finished the bulk update of p - 2 (event bulk), strips p + 4 and
+//      p + 5 in one launch;
+//   X: strips p + 6 and beyond (the bulk update, event bulk).
+// X then runs the bulk updates back to back: nothing it waits for is behind
+// its own previous launch, and S and Y do their work beside it. Trail A
+// applies p - 1 and p for odd p and p alone for even p. It waits for Y's
+// strip-(p + 1) update of p - 1 (strip2) for even p, and of p - 2 (strip3)
+// for odd p. Each strip's updates form one chain: the bulk update of p - 6
+// or p - 4 (X), Y's two-strip update of p - 4 or p - 2 (after that bulk
+// update), Y's strip update of p - 2 or p (Y's order), trail A (its wait).
+// A step waits, through this chain, for the bulk update that read the panel
+// buffer it overwrites (seven buffers: step p + 7 overwrites p's).
+// In both forms each auxiliary stream runs in order, so a wait also covers
+// every kernel enqueued on that stream before the one waited for. Every
+// strip receives every earlier super-panel exactly once before its step. U
+// is the same to the bit in both forms: each element sees the same fp64
+// MFMA sequence.
+// Measured (factor alone): d = 12288, 27.9 ms; 29.0 ms when X itself did
+// strips p + 2 to p + 5 between two bulk updates (one auxiliary stream);
+// 30.6 ms with that and 16 k per chunk in the bulk update. d = 11008: 21.0,
+// 21.9, 23.4 ms. d = 4096: 2.33 ms single, 2.43 ms paired (more launches per
+// two super-panels).
 constexpr int PAIR_MIN_D = 8192;
 extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* U, float* lambda_out, int32_t* info,
                                  void* ws, size_t ws_bytes, void* stream) {
@@ -883,6 +908,7 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
   AuxCtx* ctx = aux_context();
 
   hipStream_t x = ctx ? ctx->aux : s;
+  hipStream_t y = ctx ? ctx->aux2 : s;
   // Under stream capture the events are recorded by hipEventRecord, whose
   // capture semantics are the documented ones; otherwise the launches of
   // trail A and of X's strip updates record their events themselves.
@@ -897,17 +923,19 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
     if ((di - s0 < KS ? di - s0 : KS) > NB) nup += 4;
   hipLaunchKernelGGL(hinv_setup, dim3(unsigned(nlow + nup)), dim3(256), 0, s, H, di, w.lam, w.A, w.R, nlow);
   if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
+  const bool paired = di >= PAIR_MIN_D;
   if (ctx) {
     if (hipEventRecord(ctx->fork, s) != hipSuccess || hipStreamWaitEvent(x, ctx->fork, 0) != hipSuccess)
       return GPTQ_E_HIP;
+    if (paired && hipStreamWaitEvent(y, ctx->fork, 0) != hipSuccess) return GPTQ_E_HIP;
   }
   auto bound = [&](int a) { return a < di ? a : di; };
-  const bool paired = di >= PAIR_MIN_D;
-  // a strip update of X, recording `ev` (by the launch when possible)
-  auto strip_update = [&](const double* LT0, const double* LT, TrailSpec sp, hipEvent_t ev) -> bool {
-    if (!launch_trail(x, w, LT0, LT, di, sp, false, by_launch ? ev : nullptr)) return false;
+  // a trailing update on stream st, recording `ev` (by the launch when possible)
+  auto update = [&](hipStream_t st, const double* LT0, const double* LT, TrailSpec sp, bool bulk,
+                    hipEvent_t ev) -> bool {
+    if (!launch_trail(st, w, LT0, LT, di, sp, bulk, by_launch ? ev : nullptr)) return false;
     if (launch_status() != GPTQ_OK) return false;
-    return !ctx || by_launch || hipEventRecord(ev, x) == hipSuccess;
+    return !ctx || by_launch || hipEventRecord(ev, st) == hipSuccess;
   };
   for (int p = 0, s0 = 0; s0 < di; ++p, s0 += KS) {
     const int s1 = bound(s0 + KS);
@@ -943,21 +971,36 @@ extern "C" int gptq_prepare_hinv(const float* H, int64_t d, double damp, float* 
         if (s3 < di) launch_trail(x, w, LTw, LTw, di, TrailSpec{s0, s1, s3, 0, 0, 0, s3, di - s3, s0}, true);
         if (ctx && hipEventRecord(ctx->strip3[p % NPANEL], x) != hipSuccess) return GPTQ_E_HIP;
       } else if (odd && s2 < di) {
-        // X: p - 1 and p applied to strip p + 2, strip p + 3, then the rest
-        // (A at and beyond s4, lower triangle; R rows from s4). It starts
-        // once trail A is done, so that trail A (on the critical path) has
-        // the GPU to itself, and overlaps the next super-panel steps.
-        if (ctx && hipStreamWaitEvent(x, ctx->chain[p % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
+        // p - 1 and p applied to the rest of the trailing matrices, once
+        // trail A is done: Y takes strips p + 2 and p + 3 (each a launch of
+        // its own, as trail A of p + 1 and p + 2 wait for them), then strips
+        // p + 4 and p + 5 after X's bulk update of p - 2 (their last other
+        // writer); X takes the lower triangle of A from s6 and R's rows from
+        // s6.
+        const int s5 = bound(s4 + KS), s6 = bound(s5 + KS);
         hipEvent_t e2 = ctx ? ctx->strip2[p % NPANEL] : nullptr, e3 = ctx ? ctx->strip3[p % NPANEL] : nullptr;
-        if (!strip_update(LT0, LTw, TrailSpec{s0, s1, s2, 0, s2, s3 - s2, s2, s3 - s2, p0}, e2)) return GPTQ_E_HIP;
-        if (!strip_update(LT0, LTw, TrailSpec{s0, s1, s3, 0, s3, s4 - s3, s3, s4 - s3, p0}, e3)) return GPTQ_E_HIP;
-        if (s4 < di) launch_trail(x, w, LT0, LTw, di, TrailSpec{s0, s1, s4, 0, 0, 0, s4, di - s4, p0}, true);
+        hipEvent_t eb = ctx ? ctx->bulk[p % NPANEL] : nullptr;
+        if (ctx && hipStreamWaitEvent(y, ctx->chain[p % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
+        if (!update(y, LT0, LTw, TrailSpec{s0, s1, s2, 0, s2, s3 - s2, s2, s3 - s2, p0}, false, e2))
+          return GPTQ_E_HIP;
+        if (!update(y, LT0, LTw, TrailSpec{s0, s1, s3, 0, s3, s4 - s3, s3, s4 - s3, p0}, false, e3))
+          return GPTQ_E_HIP;
+        if (s4 < di) {
+          if (ctx && p >= 3 && hipStreamWaitEvent(y, ctx->bulk[(p - 2) % NPANEL], 0) != hipSuccess)
+            return GPTQ_E_HIP;
+          launch_trail(y, w, LT0, LTw, di, TrailSpec{s0, s1, s4, 0, s4, s6 - s4, s4, s6 - s4, p0}, false);
+        }
+        if (ctx && hipStreamWaitEvent(x, ctx->chain[p % NPANEL], 0) != hipSuccess) return GPTQ_E_HIP;
+        if (!update(x, LT0, LTw, TrailSpec{s0, s1, s6, 0, 0, 0, s6, di - s6, p0}, true, eb)) return GPTQ_E_HIP;
       }
     }
     if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
   }
   if (ctx) {
     if (hipEventRecord(ctx->join, x) != hipSuccess || hipStreamWaitEvent(s, ctx->join, 0) != hipSuccess)
+      return GPTQ_E_HIP;
+    if (paired &&
+        (hipEventRecord(ctx->join2, y) != hipSuccess || hipStreamWaitEvent(s, ctx->join2, 0) != hipSuccess))
       return GPTQ_E_HIP;
   }
   hipLaunchKernelGGL(hinv_write_u, dim3(2048), dim3(256), 0, s, w.R, di, U);

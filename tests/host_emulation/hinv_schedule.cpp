@@ -112,7 +112,7 @@ int check(int d, bool captured) {
         e.step = g.k0 / KS;
         e.strips.push_back(e.step);
         e.writes = int((g.LT - w.LT) / (size_t(KS) * d));
-      } else if (!trail_effect<128, 16>(it, w.LT, d, e) && !trail_effect<64, 16>(it, w.LT, d, e) &&
+      } else if (!trail_effect<128, 8>(it, w.LT, d, e) && !trail_effect<64, 16>(it, w.LT, d, e) &&
                  !trail_effect<64, 32>(it, w.LT, d, e) && !trail_effect<32, 32>(it, w.LT, d, e)) {
         e.all = true;  // setup, lambda, write_u
       }
