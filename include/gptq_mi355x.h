@@ -247,15 +247,26 @@ int gptq_dequantize(const uint32_t* packed, const float* scales, const int32_t* 
  *              columns; bits 2, 3, 4 or 8).
  *   X          device fp16, n_tokens rows of d_in values, row stride ldx.
  *   Y          device fp16, n_tokens x d_out, row stride ldy >= d_out.
+ *   ws         device workspace of gptq_dequant_gemm_workspace_size(d_out,
+ *              d_in, n_tokens) bytes, or NULL. With a workspace and d_in a
+ *              multiple of 128, the weights are dequantized once into it
+ *              (K-major fp16, the same values) and X is copied K-major beside
+ *              them; the product then runs on both from there (the form for
+ *              large token batches). Without one, or for other d_in, the
+ *              weights are dequantized inside the product kernel per token
+ *              tile. Both use the same fp16 weights; their fp32 sums run in
+ *              different orders inside each 16-K MFMA step.
  * Runs on `stream`; nothing is allocated; n_tokens = 0 does nothing.
  * Errors: sizes < 1, NULL pointers, ldx < d_in, ldy < d_out, bad bits,
  * group_size 0 or < -1, relu not 0 or 1 -> GPTQ_E_INVALID_ARG; d_in not a
  * multiple of 32, group_size not -1 or a multiple of 64, X not 16-byte
- * aligned or ldx not a multiple of 8 -> GPTQ_E_UNSUPPORTED.
+ * aligned or ldx not a multiple of 8 -> GPTQ_E_UNSUPPORTED; ws given with
+ * ws_bytes below the size query -> GPTQ_E_WORKSPACE.
  * ---------------------------------------------------------------------- */
 int gptq_dequant_gemm(const uint32_t* packed, const float* scales, const int32_t* zeros, int64_t d_out,
                       int64_t d_in, int bits, int64_t group_size, const void* X, int64_t n_tokens,
-                      int64_t ldx, void* Y, int64_t ldy, int relu, void* stream);
+                      int64_t ldx, void* Y, int64_t ldy, int relu, void* ws, size_t ws_bytes, void* stream);
+size_t gptq_dequant_gemm_workspace_size(int64_t d_out, int64_t d_in, int64_t n_tokens);
 
 /* ------------------------------------------------------------------------
  * Column order: act-order permutation.

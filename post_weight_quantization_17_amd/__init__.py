@@ -53,8 +53,10 @@ _SIGNATURES = {
     ),
     "gptq_dequant_gemm": (
         _c_int,
-        [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_int, _c_ptr],
+        [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_int, _c_ptr,
+         _c_size, _c_ptr],
     ),
+    "gptq_dequant_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "gptq_dequant_matvec": (
         _c_int,
         [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_i64, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr],
@@ -441,11 +443,18 @@ def gptq_dequant_matvec(
     return y.squeeze(0) if x.dim() == 1 else y
 
 
+def gptq_dequant_gemm_workspace_size(d_out: int, d_in: int, n_tokens: int) -> int:
+    return load().gptq_dequant_gemm_workspace_size(d_out, d_in, n_tokens)
+
+
 def gptq_dequant_gemm(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, d_in: int, bits: int,
                       group_size: int, X: torch.Tensor, relu: bool = False,
-                      Y: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      Y: Optional[torch.Tensor] = None, fused: bool = False,
+                      ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y = act(X What^T) (fp16) for the packed layer [d_out rows] and fp16
-    tokens X [n, d_in]; act is ReLU with ``relu``."""
+    tokens X [n, d_in]; act is ReLU with ``relu``. By default a workspace is
+    passed (weights dequantized once, K-major operands); ``fused`` runs the
+    per-tile dequantizing kernel without one. Both give the same bits."""
     for n, t in (("packed", packed), ("scales", scales), ("zeros", zeros), ("X", X)):
         _on_gpu(n, t)
     if X.dtype != torch.float16 or X.dim() != 2 or X.stride(1) != 1 or X.shape[1] != d_in:
@@ -458,9 +467,15 @@ def gptq_dequant_gemm(packed: torch.Tensor, scales: torch.Tensor, zeros: torch.T
         raise ValueError("Y must be fp16 [n, d_out] with unit column stride")
     ldx = X.stride(0) if n > 1 else d_in
     ldy = Y.stride(0) if n > 1 else d_out
+    lib = load()
+    wsp, wsb = None, 0
+    if not fused and n > 0:
+        wsb = lib.gptq_dequant_gemm_workspace_size(d_out, d_in, n)
+        ws = _workspace(wsb, X.device, ws)
+        wsp, wsb = _ptr(ws), ws.numel() * ws.element_size()
     _check(
         "gptq_dequant_gemm",
-        load().gptq_dequant_gemm(_ptr(packed), _ptr(scales), _ptr(zeros), d_out, d_in, bits, group_size, _ptr(X), n,
-                                 ldx, _ptr(Y), ldy, int(bool(relu)), _stream()),
+        lib.gptq_dequant_gemm(_ptr(packed), _ptr(scales), _ptr(zeros), d_out, d_in, bits, group_size, _ptr(X), n,
+                              ldx, _ptr(Y), ldy, int(bool(relu)), wsp, wsb, _stream()),
     )
     return Y

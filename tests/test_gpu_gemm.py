@@ -66,14 +66,48 @@ def check_gemm(y, X, packed, scales, zeros, d_in, bits, group, relu):
     (300, 70, 1376, 4, -1, False),  # d_in = 43 x 32: a last K tile of 32 columns
     (129, 33, 96, 2, -1, True),
 ])
-def test_dequant_gemm_parity(gpu, n, d_out, d_in, bits, group, relu):
-    say("dequant gemm", n, d_out, d_in, bits, group, relu)
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "two_pass"])
+def test_dequant_gemm_parity(gpu, n, d_out, d_in, bits, group, relu, fused):
+    say("dequant gemm", n, d_out, d_in, bits, group, relu, "fused" if fused else "workspace")
     packed, scales, zeros = layer(d_out, d_in, bits, group, n + d_out)
     X = tokens(n, d_in, d_in + bits)
     y = gpu.gptq_dequant_gemm(gpu_tensor(packed.view(np.int32)), gpu_tensor(scales), gpu_tensor(zeros), d_in, bits,
-                              group, gpu_tensor(X), relu=relu)
+                              group, gpu_tensor(X), relu=relu, fused=fused)
     torch.cuda.synchronize()
     check_gemm(y.cpu().numpy(), X, packed, scales, zeros, d_in, bits, group, relu)
+
+
+@pytest.mark.parametrize("n,d_out,d_in,bits,group,relu", [
+    (256, 256, 128, 4, 128, False),    # one tile, one block of 128 K
+    (1000, 300, 512, 3, 128, True),    # ragged tokens and rows, four stages
+    (2048, 768, 384, 2, -1, False),    # several tiles both ways, 12 stages
+    (513, 520, 640, 8, 64, True),      # ragged, 8-bit, groups of 64
+    (4096, 1024, 1024, 4, 128, True),  # token tiles a multiple of 8 (XCD order)
+])
+def test_dequant_gemm_two_pass_equals_fused(gpu, n, d_out, d_in, bits, group, relu):
+    """The workspace form (weights dequantized once, K-major operands, the
+    Hessian's pipeline) on shapes it takes, against the oracle's bound. It
+    uses the same fp16 weights as the fused form; the fp32 sums run in a
+    different order inside each 16-K MFMA step, so the two may differ by
+    rounding: the fraction of equal outputs is reported. The workspace starts
+    NaN-filled, so a read of anything the pre-passes did not write shows."""
+    say("dequant gemm two-pass", n, d_out, d_in, bits, group, relu)
+    packed, scales, zeros = layer(d_out, d_in, bits, group, 7 * n + d_out)
+    X = tokens(n, d_in, d_in + 3 * bits)
+    P, S, Z, XT = gpu_tensor(packed.view(np.int32)), gpu_tensor(scales), gpu_tensor(zeros), gpu_tensor(X)
+    need = gpu.gptq_dequant_gemm_workspace_size(d_out, d_in, n)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN-filled fp16: nothing unwritten is read
+    y2 = gpu.gptq_dequant_gemm(P, S, Z, d_in, bits, group, XT, relu=relu, ws=ws)
+    y1 = gpu.gptq_dequant_gemm(P, S, Z, d_in, bits, group, XT, relu=relu, fused=True)
+    torch.cuda.synchronize()
+    a, b = y2.cpu().numpy(), y1.cpu().numpy()
+    check_gemm(a, X, packed, scales, zeros, d_in, bits, group, relu)
+    say(f"  two-pass equal to fused: {float(np.mean(a == b)):.6f}")
+    lib = gpu.load()
+    Y = torch.empty((n, d_out), dtype=torch.float16, device=DEV)
+    assert lib.gptq_dequant_gemm(P.data_ptr(), S.data_ptr(), Z.data_ptr(), d_out, d_in, bits, group, XT.data_ptr(), n,
+                                 d_in, Y.data_ptr(), d_out, int(relu), ws.data_ptr(), need - 1,
+                                 None) == gpu.GPTQ_E_WORKSPACE
 
 
 def test_dequant_gemm_strided_and_bad_arguments(gpu):
@@ -95,8 +129,8 @@ def test_dequant_gemm_strided_and_bad_arguments(gpu):
     lib = gpu.load()
     p = Ybig.data_ptr()
     x = Xbig.data_ptr()
-    assert lib.gptq_dequant_gemm(p, p, p, 8, 100, 4, -1, x, 4, 320, p, 8, 0, None) == gpu.GPTQ_E_UNSUPPORTED  # d_in % 32
-    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, 32, x, 4, 320, p, 8, 0, None) == gpu.GPTQ_E_UNSUPPORTED  # group
-    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 5, -1, x, 4, 320, p, 8, 0, None) == gpu.GPTQ_E_INVALID_ARG  # bits
-    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 100, p, 8, 0, None) == gpu.GPTQ_E_INVALID_ARG  # ldx
-    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 320, p, 8, 2, None) == gpu.GPTQ_E_INVALID_ARG  # relu
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 100, 4, -1, x, 4, 320, p, 8, 0, None, 0, None) == gpu.GPTQ_E_UNSUPPORTED  # d_in % 32
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, 32, x, 4, 320, p, 8, 0, None, 0, None) == gpu.GPTQ_E_UNSUPPORTED  # group
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 5, -1, x, 4, 320, p, 8, 0, None, 0, None) == gpu.GPTQ_E_INVALID_ARG  # bits
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 100, p, 8, 0, None, 0, None) == gpu.GPTQ_E_INVALID_ARG  # ldx
+    assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 320, p, 8, 2, None, 0, None) == gpu.GPTQ_E_INVALID_ARG  # relu
