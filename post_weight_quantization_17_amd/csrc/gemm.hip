@@ -297,23 +297,32 @@ __device__ __forceinline__ half8 kfrag(const unsigned char* lds, int off) {
   return __builtin_bit_cast(half8, v);
 }
 
-// 64 x 64 blocks through LDS: XK[c][t] = X[t][c] for t < n, 0 for n <= t < ldk.
+// 128 tokens x 64 channels per workgroup through LDS, 16-byte global reads
+// and writes: XK[c][t] = X[t][c] for t < n, 0 for n <= t < ldk. Needs X
+// 16-byte aligned with ldx % 8 == 0, d_in % 64 == 0 and ldk % 128 == 0.
 __global__ void __launch_bounds__(256)
 kmajor_transpose_f16(const __half* __restrict__ X, int64_t n, int d_in, int64_t ldx, __half* __restrict__ XK,
                      int64_t ldk) {
-  __shared__ unsigned short t[64][66];
-  const int64_t t0 = int64_t(blockIdx.x) * 64;
+  __shared__ __attribute__((aligned(16))) unsigned short t[128][72];
+  const int64_t t0 = int64_t(blockIdx.x) * 128;
   const int c0 = int(blockIdx.y) * 64;
   const int tid = threadIdx.x;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;  // token r, channel c (channels contiguous)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = tid + 256 * k, r = idx >> 3, q = idx & 7;  // token r, channels 8q .. 8q + 7
     const int64_t tok = t0 + r;
-    t[r][c] = (tok < n && c0 + c < d_in) ? __half_as_ushort(X[tok * ldx + c0 + c]) : (unsigned short)0;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (tok < n) v = *reinterpret_cast<const uint4*>(X + tok * ldx + c0 + 8 * q);
+    *reinterpret_cast<uint4*>(&t[r][8 * q]) = v;
   }
   __syncthreads();
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int c = e >> 6, r = e & 63;  // channel c, token r (tokens contiguous)
-    if (c0 + c < d_in && t0 + r < ldk) XK[int64_t(c0 + c) * ldk + t0 + r] = __ushort_as_half(t[r][c]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = tid + 256 * k, c = idx & 63, p = idx >> 6;  // channel c, tokens 8p .. 8p + 7
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = uint32_t(t[8 * p + 2 * i][c]) | (uint32_t(t[8 * p + 2 * i + 1][c]) << 16);
+    *reinterpret_cast<uint4*>(XK + int64_t(c0 + c) * ldk + t0 + 8 * p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -387,12 +396,33 @@ gemm_kmajor_f16(const __half* __restrict__ WK, int64_t ldw, const __half* __rest
   __shared__ __attribute__((aligned(16))) unsigned char lds2[K_STAGE];
   __shared__ __attribute__((aligned(16))) unsigned char lds3[K_STAGE];
 
-  // Work order as in the fused kernel: XCD x takes token tiles x, x + 8, ...,
-  // each across all weight tiles, so a token tile stays in one L2.
+  // Work order. Workgroups go to the 8 XCDs round-robin (b % 8), 32 at a
+  // time per XCD (one per CU). When the token tiles divide into 64, XCD x
+  // takes token tiles x, x + 8, ... in blocks of 8, and walks each block
+  // across the weight tiles 4 at a time: the 32 workgroups an XCD runs
+  // together share 8 token panels and 4 weight panels in its L2 (12 panels
+  // for 32 tiles, against 33 when one token tile meets 32 weight tiles).
+  // Otherwise XCD x takes token tiles x, x + 8, ... each across all weight
+  // tiles (as the fused kernel), or consecutive workgroups share a token tile.
   int tn;
   int64_t tm;
   const unsigned b = blockIdx.x;
-  if (n_tiles_m8) {
+  if (n_tiles_m8 == 2) {
+    const unsigned j = b >> 3, x = b & 7, nt = unsigned(n_tiles_n);
+    const unsigned tb = j / (8u * nt), rem = j % (8u * nt);  // token block, place in it
+    const unsigned full = nt / 4u;                            // whole blocks of 4 weight tiles
+    unsigned tl, wn;
+    if (rem < 32u * full) {
+      wn = (rem / 32u) * 4u + (rem % 4u);
+      tl = tb * 8u + (rem % 32u) / 4u;
+    } else {
+      const unsigned w = nt - 4u * full, r2 = rem - 32u * full;  // the last, narrower block
+      wn = 4u * full + r2 % w;
+      tl = tb * 8u + r2 / w;
+    }
+    tm = int64_t(tl) * 8 + x;
+    tn = int(wn);
+  } else if (n_tiles_m8) {
     const unsigned j = b >> 3;
     tm = int64_t(j / unsigned(n_tiles_n)) * 8 + (b & 7);
     tn = int(j % unsigned(n_tiles_n));
@@ -631,14 +661,14 @@ extern "C" int gptq_dequant_gemm(const uint32_t* packed, const float* scales, co
           break;
       }
       if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
-      hipLaunchKernelGGL(kmajor_transpose_f16, dim3(unsigned(kp.ldk / 64), unsigned((d_in + 63) / 64)), dim3(256), 0,
+      hipLaunchKernelGGL(kmajor_transpose_f16, dim3(unsigned(kp.ldk / 128), unsigned(d_in / 64)), dim3(256), 0,
                          s, static_cast<const __half*>(X), n_tokens, int(d_in), ldx, XK, kp.ldk);
       if (launch_status() != GPTQ_OK) return GPTQ_E_HIP;
       const int64_t km = kp.ldk / K_T, kn = kp.ldw / K_T;
       const int vec = (reinterpret_cast<uintptr_t>(Y) % 8 == 0 && ldy % 4 == 0) ? 1 : 0;
       hipLaunchKernelGGL(gemm_kmajor_f16, dim3(unsigned(km * kn)), dim3(256), 0, s, WK, kp.ldw, XK, kp.ldk,
                          int(d_in / K_BK), int(d_out), n_tokens, static_cast<__half*>(Y), ldy, relu, vec, int(kn),
-                         km % 8 == 0 ? 1 : 0);
+                         km % 64 == 0 ? 2 : (km % 8 == 0 ? 1 : 0));
       return launch_status();
     }
   }

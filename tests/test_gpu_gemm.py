@@ -83,6 +83,8 @@ def test_dequant_gemm_parity(gpu, n, d_out, d_in, bits, group, relu, fused):
     (2048, 768, 384, 2, -1, False),    # several tiles both ways, 12 stages
     (513, 520, 640, 8, 64, True),      # ragged, 8-bit, groups of 64
     (4096, 1024, 1024, 4, 128, True),  # token tiles a multiple of 8 (XCD order)
+    (16384, 1100, 128, 4, 128, True),  # token tiles a multiple of 64: blocked XCD order, a last block of 1 weight tile
+    (16384, 300, 256, 3, -1, False),   # blocked order with only a narrower block (2 weight tiles)
 ])
 def test_dequant_gemm_two_pass_equals_fused(gpu, n, d_out, d_in, bits, group, relu):
     """The workspace form (weights dequantized once, K-major operands, the
