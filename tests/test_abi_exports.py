@@ -71,3 +71,21 @@ def test_workspace_sizes(lib):
     # sweep: fp32 working copy of W plus per-workgroup loss partials
     q = lib.gptq_quantize_layer_workspace_size(i64(4096), i64(4096), 4, i64(128), i64(128))
     assert q >= 4096 * 4096 * 4 and q < 4096 * 4096 * 4 + 4096
+
+
+def test_dequant_gemm_workspace_size(lib):
+    """The two-pass GEMM's workspace: the K-major fp16 weights [d_in][d_out rounded up to 256] and the K-major
+    fp16 tokens [d_in][n rounded up to 256], each aligned to 256 bytes."""
+    f = lib.gptq_dequant_gemm_workspace_size
+    f.restype = ctypes.c_size_t
+    i64 = ctypes.c_int64
+
+    def expect(d_out, d_in, n):
+        up = lambda x, a: (x + a - 1) // a * a
+        return up(2 * d_in * up(d_out, 256), 256) + up(2 * d_in * up(n, 256), 256)
+
+    for d_out, d_in, n in [(11008, 4096, 262144), (4096, 11008, 262144), (1, 128, 1), (300, 640, 1000)]:
+        assert f(i64(d_out), i64(d_in), i64(n)) == expect(d_out, d_in, n)
+    assert f(i64(11008), i64(4096), i64(262144)) == 2 * 4096 * (11008 + 262144)  # 2.2 GB at the MLP up product
+    assert f(i64(0), i64(128), i64(10)) == 0
+    assert f(i64(8), i64(0), i64(10)) == 0
