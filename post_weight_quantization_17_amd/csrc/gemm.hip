@@ -7,7 +7,11 @@
 // the fly. What = s (code - z) per group (astro-blog survey, section 1.2),
 // held as fp16 to run: the fp32 product s (code - z), rounded to fp16.
 //
-// Design (gfx950), one workgroup of 8 waves (two per SIMD) per 256-token x
+// Two forms: the fused kernel below (no workspace; the weights are
+// dequantized inside the product, tile by tile) and, further down, a
+// two-pass form for large token batches that takes a caller workspace.
+//
+// Fused design (gfx950), one workgroup of 8 waves (two per SIMD) per 256-token x
 // 128-weight-row output tile, K (d_in) in tiles of 64:
 //  * X tiles [256 tokens][64] fp16 move straight from HBM into LDS
 //    (global_load_lds, 16 bytes per lane) in three stages, the tile for
@@ -266,10 +270,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 // ---------------------------------------------------------------------------
 // Two-pass form for compute-bound batches (a caller workspace is given and
-// d_in is a multiple of 128). The weights are dequantized once per call, not
-// once per token tile: at one wave per SIMD the per-tile dequantization of
-// the fused kernel above cannot hide behind the MFMAs. Both operands are laid
-// out K-major in the workspace, so the product runs the Hessian's pipeline
+// d_in is a multiple of 128). The fused kernel above rebuilds each weight
+// tile for every 256-token tile; with the 128 x 128 wave tiles the MFMA rate
+// needs (one wave per SIMD) that rebuild does not hide behind the MFMAs, so
+// here the weights are dequantized once per call. Both operands are laid out
+// K-major in the workspace, so the product runs the Hessian's pipeline
 // (direct-to-LDS loads, transposing LDS reads, one barrier per 32 K):
 //   kmajor_transpose_f16:  X [n][d_in] -> XK [d_in][ldk]   (tokens >= n: 0)
 //   dequant_kmajor_f16:    packed -> WK [d_in][ldw] = fp16(s (c - z))
