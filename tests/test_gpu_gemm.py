@@ -136,3 +136,42 @@ def test_dequant_gemm_strided_and_bad_arguments(gpu):
     assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 5, -1, x, 4, 320, p, 8, 0, None, 0, None) == gpu.GPTQ_E_INVALID_ARG  # bits
     assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 100, p, 8, 0, None, 0, None) == gpu.GPTQ_E_INVALID_ARG  # ldx
     assert lib.gptq_dequant_gemm(p, p, p, 8, 128, 4, -1, x, 4, 320, p, 8, 2, None, 0, None) == gpu.GPTQ_E_INVALID_ARG  # relu
+
+
+@pytest.mark.parametrize("name,relu", [("mlp_up_11008x4096_4bit_g128", True), ("mlp_down_4096x11008_4bit_g128", False)])
+def test_dequant_gemm_full_size_sampled(gpu, name, relu):
+    """The quantized layer at the MLP block's full size (262144 tokens of the
+    configuration's activations, its weight shape, 4-bit g128), both forms,
+    in the launch configuration the benchmark's pipeline leg times. The
+    oracle computes 64 seeded tokens x 256 seeded weight rows one by one, to
+    the same fp32-summation bound and >= 99% equality as the small cases."""
+    from workload import CONFIGS, activation_chunks
+    cfg = CONFIGS[name]
+    d_out, d_in, n, bits, group = cfg.d_row, cfg.d_col, cfg.n_tokens, cfg.bits, cfg.group_size
+    say("dequant gemm full size", name, n, d_out, d_in, bits, group, relu)
+    r = np.random.default_rng(1234)
+    toks = np.sort(r.choice(n, 64, replace=False))
+    rows = np.sort(r.choice(d_out, 256, replace=False))
+    # a seeded packed layer (random words: every code value occurs), scales and zeros
+    nw = d_in * bits // 32
+    packed = r.integers(0, 2**32, size=(d_out, nw), dtype=np.uint64).astype(np.uint32)
+    ng = -(-d_in // group)
+    scales = r.uniform(0.001, 0.03, size=(d_out, ng)).astype(np.float32)
+    zeros = r.integers(0, 1 << bits, size=(d_out, ng)).astype(np.int32)
+    Xd = torch.empty((n, d_in), dtype=torch.float16, device=DEV)
+    Xs = np.empty((64, d_in), dtype=np.float16)
+    t = 0
+    for ch in activation_chunks(cfg, threads=16):
+        Xd[t:t + ch.shape[0]].copy_(torch.from_numpy(ch))
+        sel = (toks >= t) & (toks < t + ch.shape[0])
+        Xs[sel] = ch[toks[sel] - t]
+        t += ch.shape[0]
+    assert t == n
+    P, S, Z = gpu_tensor(packed.view(np.int32)), gpu_tensor(scales), gpu_tensor(zeros)
+    ti, ri = torch.from_numpy(toks).to(DEV), torch.from_numpy(rows).to(DEV)
+    for fused in (False, True):
+        y = gpu.gptq_dequant_gemm(P, S, Z, d_in, bits, group, Xd, relu=relu, fused=fused)
+        ys = y.index_select(0, ti).index_select(1, ri).cpu().numpy()
+        del y
+        torch.cuda.synchronize()
+        check_gemm(ys, Xs, packed[rows], scales[rows], zeros[rows], d_in, bits, group, relu)
