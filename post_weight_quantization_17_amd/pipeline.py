@@ -14,7 +14,9 @@ run to produce the next block's inputs. Two pieces of that:
 
 Every step runs in the library's kernels, the quantized layers included
 (``gptq_dequant_gemm``: tokens x packed weights on the fp16 MFMA with the
-ReLU in its epilogue). torch only provides device memory and streams.
+ReLU in its epilogue; with its workspace, the weights are dequantized once
+and both operands are taken K-major). torch only provides device memory,
+workspaces and streams.
 """
 
 from __future__ import annotations
