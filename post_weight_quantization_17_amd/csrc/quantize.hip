@@ -20,8 +20,9 @@
 //      every lane of the row takes the same rounding decision, and each lane
 //      applies the rank-1 update to its own columns (U row q from LDS);
 //   3. writes codes, packs the block's 32-bit words from an LDS copy of the
-//      codes (128 * bits is a whole number of words), and stores the errors
-//      e = err / U_qq in LDS;
+//      codes (128 * bits is a whole number of words), and stores the
+//      negated errors -e = -err / U_qq in LDS (the update's A operand as it
+//      is used: no negation and no wait on the LDS read beside the MFMAs);
 //   4. applies W[rows, i2:] -= E U[blk, i2:] with v_mfma_f32_16x16x4f32 (the
 //      workgroup's 16 rows are exactly one MFMA M tile; each lane's 4
 //      consecutive output columns make W and U accesses 16-byte vectors),
@@ -197,7 +198,7 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
     float an[RG];  // RG = 2: the next k-step's A operands
     if constexpr (RG > 1) {
 #pragma unroll
-      for (int g = 0; g < RG; ++g) an[g] = -eb[16 * g * EP];
+      for (int g = 0; g < RG; ++g) an[g] = eb[16 * g * EP];
     }
     // One group of KS4 k-steps (128 rows of U). In every group but the
     // chunk's last, all prefetches stay in this chunk.
@@ -211,7 +212,7 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
         else if (more)
           ring[t % RING] = ldb(ch + 1, t + RING - KS4);
         if constexpr (RG == 1) {
-          const float at = -eb[4 * T];  // A operand: row li, k = 4T + lk
+          const float at = eb[4 * T];  // A operand: row li, k = 4T + lk
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[0][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(at, b[v], acc[0][v], 0, 0, 0);
         } else {
@@ -220,7 +221,7 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
           for (int g = 0; g < RG; ++g) a[g] = an[g];
           if (!last || t + 1 < KS4) {
 #pragma unroll
-            for (int g = 0; g < RG; ++g) an[g] = -eb[16 * g * EP + 4 * (T + 1)];
+            for (int g = 0; g < RG; ++g) an[g] = eb[16 * g * EP + 4 * (T + 1)];
           }
           asm volatile("" ::: "memory");  // each step's reads stay in their step (no hoisting)
 #pragma unroll
@@ -425,7 +426,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
       // Every lane of the row holds the same code and error: all 16 store
       // the same value to the row's LDS slot, so no owner test is needed.
       Cs[rloc][q] = uint8_t(c);
-      Es[rloc][kk0 + q] = e;
+      Es[rloc][kk0 + q] = -e;
       if constexpr (q + 1 < QB) {
 #pragma unroll
         for (int mm = (q + 1) / 16; mm < QM; ++mm) uc[mm] = un[mm];
@@ -520,7 +521,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
             for (int t = 0; t < RING; ++t) ring[t] = ldb(t);
 #pragma unroll
             for (int t = 0; t < QB / 4; ++t) {
-              const float at = -Es[li][ec0 + QB * sb + 4 * t + lk];  // A operand: row li, k = 128 sb + 4t + lk
+              const float at = Es[li][ec0 + QB * sb + 4 * t + lk];  // A operand: row li, k = 128 sb + 4t + lk
               const floatx4 b = ring[t % RING];
               if (t + RING < QB / 4) ring[t % RING] = ldb(t + RING);
 #pragma unroll
@@ -587,7 +588,7 @@ gptq_sweep(const WT* __restrict__ W, float* __restrict__ Wf, const float* __rest
         for (int t = 0; t < RING; ++t) ring[t] = ldb(t);
 #pragma unroll
         for (int t = 0; t < QB / 4; ++t) {
-          const float at = -Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
+          const float at = Es[li][4 * t + lk];  // A operand: row li, k = 4t + lk
           const floatx4 b = ring[t % RING];
           if (t + RING < QB / 4) ring[t % RING] = ldb(t + RING);
 #pragma unroll
