@@ -170,9 +170,11 @@ __device__ __forceinline__ void trailing_update_whole(const WT* __restrict__ W, 
       for (int r = 0; r < 4; ++r) v[g][r] = first ? load4(w0 + wso(g, r, ch)) : load4(f0 + wso(g, r, ch));
   };
   // U k-steps in flight. RG = 2 reads its A operands from LDS one k-step
-  // ahead instead of keeping all 64 of them in registers, which leaves room
-  // for a deeper ring.
-  constexpr int RING = RG == 1 ? 8 : sizeof(WT) == 2 ? 16 : 8;
+  // ahead instead of keeping all 64 of them in registers. Measured at
+  // 49152 x 12288 (32 rows, fp16 W): a ring of 8 k-steps, 61.2 ms; 16,
+  // 62.8 ms (256 VGPRs, and the compiler moves accumulators between
+  // registers); 4, 63.2 ms.
+  constexpr int RING = 8;
   constexpr int KS4 = QB / 4;             // k-steps per 128 rows of U
   // Step t of a 32-step group uses slot t % RING, and the last RING steps of
   // a chunk prefetch the next chunk's first steps into their own slots: RING
